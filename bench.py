@@ -1,0 +1,248 @@
+"""Frame-step throughput of the 24-block ViT-L-shaped stream on one MI355X.
+
+One step = one new frame through all 24 blocks: per block, append its K/V
+(HIP scatter), evict and plan once (host; one small table upload), and paged
+attention (HIP, bf16 MFMA).  Shapes: 1369 patch + 6 special tokens per frame,
+16 heads x 64, scale_frames 8, sliding_window 64, bf16 unit-normal inputs.
+
+Setup (untimed): the 8-frame first step and 64 single frames (F = 72, the
+window full), then W warm-up steps; then K timed steps.  The defaults stream
+the full 1000 frames (F = 81..1000 timed).  Inputs: 8 distinct seeded input
+sets per block, drawn up front and resident in HBM, cycled over the steps.
+
+Printed: one JSON line with frames/s (value), the attention kernel's roofline
+(algorithmic FLOPs per launch / launch time from HIP events on the launch
+stream, against the bf16 dense MFMA peak) and the CPU oracle timed on a
+bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+N_INPUT_SETS = 8
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=920)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--splits", type=int, default=0, help="force the key-range split count")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the path would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_312_amd as lbm
+    import workloads
+
+    cfg = workloads.get_config("vitl_24_block_frame_step")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, H, D, T = cfg.num_blocks, cfg.num_heads, cfg.head_dim, cfg.tokens_per_frame
+    fields = workloads.lbm_config_fields(cfg, num_splits=args.splits)
+    cache = lbm.PagedKVCache(lbm.make_config(**fields), dev)
+    stream = torch.cuda.current_stream()
+
+    # inputs: the first step, then N_INPUT_SETS single-frame sets per block
+    init = [workloads.gen_step_qkv(cfg, b, 0, cfg.initial_frames, dev) for b in range(B)]
+    sets = [[workloads.gen_step_qkv(cfg, b, 1 + i, 1, dev) for b in range(B)]
+            for i in range(N_INPUT_SETS)]
+    outs = [torch.empty((T, H, D), dtype=torch.bfloat16, device=dev) for _ in range(B)]
+    out_init = torch.empty((cfg.initial_frames * T, H, D), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def frame_step(inputs, out_bufs, nq, ev=None):
+        for b in range(B):
+            q, k, v = inputs[b]
+            cache.append_frame(b, k, v)
+            if b == 0:
+                cache.evict_frames()
+                cache.plan(nq)
+            if ev is not None:
+                ev[b][0].record(stream)
+            cache.run(b, q, out_bufs[b])
+            if ev is not None:
+                ev[b][1].record(stream)
+
+    frame_step(init, [out_init] * B, cfg.initial_frames * T)
+    F = cfg.initial_frames
+    step_idx = 0
+    while F < cfg.scale_frames + cfg.sliding_window:
+        frame_step(sets[step_idx % N_INPUT_SETS], outs, T)
+        F += 1
+        step_idx += 1
+    for _ in range(args.warmup):
+        frame_step(sets[step_idx % N_INPUT_SETS], outs, T)
+        F += 1
+        step_idx += 1
+    torch.cuda.synchronize()
+    F_first = F + 1
+
+    # timed region: K steps; attention launches bracketed by events on the
+    # launch stream for the roofline figure
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in range(B)] for _ in range(args.steps)]
+    kv_lens = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        frame_step(sets[step_idx % N_INPUT_SETS], outs, T, ev[i])
+        F += 1
+        step_idx += 1
+        kv_lens.append(cache.get_plan()[0] if i == 0 else kv_lens[-1] + cfg.special_per_frame)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    splits = cache.num_splits()
+    assert cache.stats()["frame_count"] == F
+
+    attn_ms = 0.0
+    flops = 0.0
+    for i in range(args.steps):
+        for b in range(B):
+            attn_ms += ev[i][b][0].elapsed_time(ev[i][b][1])
+        flops += B * 4.0 * T * kv_lens[i] * H * D
+    n_launch = args.steps * B
+    avg_launch_ms = attn_ms / n_launch
+    achieved_tflops = flops / (attn_ms * 1e-3) / 1e12
+    ms_per_step = elapsed * 1e3 / args.steps
+    fps = args.steps / elapsed
+
+    # append bandwidth: one extra timed pass of 24 appends into the live step
+    # is not possible without a new reservation, so time the appends of one
+    # more full step with events around each
+    e_app = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+             for _ in range(B)]
+    inputs = sets[step_idx % N_INPUT_SETS]
+    for b in range(B):
+        q, k, v = inputs[b]
+        e_app[b][0].record(stream)
+        cache.append_frame(b, k, v)
+        e_app[b][1].record(stream)
+        if b == 0:
+            cache.evict_frames()
+            cache.plan(T)
+        cache.run(b, q, outs[b])
+    torch.cuda.synchronize()
+    app_ms = sum(a.elapsed_time(e) for a, e in e_app) / B
+    app_bytes = 2 * 2 * T * H * D * 2  # K and V rows, read + write, bf16
+    append_gbps = app_bytes / (app_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "frames/sec per 24-block step at window 64 + attention MFMA util vs bf16 peak",
+        "value": round(fps, 3),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "blocks": B, "heads": H, "head_dim": D,
+                   "patches_per_frame": cfg.patches_per_frame,
+                   "special_per_frame": cfg.special_per_frame, "scale_frames": cfg.scale_frames,
+                   "sliding_window": cfg.sliding_window, "timed_frames": [F_first, F],
+                   "kv_len": [kv_lens[0], kv_lens[-1]], "query_tokens": T,
+                   "key_splits": splits},
+        "roofline": {"bound": "mfma", "achieved": round(achieved_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_bf16_d64_kernel", "avg_launch_ms": round(avg_launch_ms, 4),
+                     "flops_per_launch_avg": flops / n_launch},
+        "append": {"bound": "hbm", "achieved": round(append_gbps, 1), "peak": PEAK_HBM_GBPS,
+                   "unit": "GB/s", "frac": round(append_gbps / PEAK_HBM_GBPS, 4),
+                   "avg_launch_ms": round(app_ms, 5), "bytes_per_launch": app_bytes},
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, init, sets, F, args.cpu_seconds)
+    cache.close()
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, init, sets, F_now, budget_s):
+    """The oracle as it stands, timed on this host on a bounded sample of one
+    steady-state frame step: block 0, the step's 1375 query rows, h heads,
+    against the full visible set at the current frame count; scaled to the
+    whole 24-block, 16-head step."""
+    import numpy as np
+    import torch
+    from oracle import StreamOracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [os.cpu_count() or 1])
+    except Exception:
+        threads = os.cpu_count() or 1
+
+    B, H, T = cfg.num_blocks, cfg.num_heads, cfg.tokens_per_frame
+
+    n0 = cfg.initial_frames
+
+    class CycledHistory:
+        """The bytes the bench appended: frames of the first step from its
+        tensors, frame f >= n0 from input set (f - n0) mod n."""
+        def __init__(self):
+            self.cache = {}
+
+        def rows(self, block, frame, lo, hi, heads=None):
+            key = ("i", block) if frame < n0 else ((frame - n0) % len(sets), block)
+            if key not in self.cache:
+                _, k, v = init[block] if frame < n0 else sets[key[0]][block]
+                self.cache[key] = (k.double().cpu().numpy(), v.double().cpu().numpy())
+            k, v = self.cache[key]
+            if frame < n0:
+                k, v = k[frame * T:(frame + 1) * T], v[frame * T:(frame + 1) * T]
+            k, v = k[lo:hi], v[lo:hi]
+            if heads is not None:
+                k, v = k[:, heads], v[:, heads]
+            return k, v
+
+    orc = StreamOracle(cfg.patches_per_frame, cfg.special_per_frame, cfg.scale_frames,
+                       cfg.sliding_window, history=CycledHistory())
+    orc.F = F_now
+    q, k, v = (t.double().cpu().numpy() for t in sets[(F_now - n0) % len(sets)][0])
+    t0 = time.perf_counter()
+    orc.step_outputs(0, q, k, v, heads=[0])
+    t1 = time.perf_counter() - t0
+    n_heads = int(max(1, min(H, budget_s // max(t1, 1e-3))))
+    t0 = time.perf_counter()
+    if n_heads > 1:
+        orc.step_outputs(0, q, k, v, heads=list(range(1, n_heads)))
+    t_rest = time.perf_counter() - t0
+    per_head = (t1 + t_rest) / n_heads
+    step_s = per_head * H * B
+    return {"value": round(1.0 / step_s, 6), "unit": "frames/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"block 0, {n_heads} of {H} heads, all {T} query rows of one frame step "
+                       f"at F={F_now + 1} (kv_len {98568 + 6 * (F_now + 1)}), fp64 numpy; "
+                       f"{t1 + t_rest:.1f} s measured, scaled x{H * B / n_heads:.0f} to the "
+                       f"24-block step ({step_s:.1f} s/frame)")}
+
+
+if __name__ == "__main__":
+    main()

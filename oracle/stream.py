@@ -39,6 +39,14 @@ class DictHistory:
     def get(self, block: int, frame: int) -> Tuple[np.ndarray, np.ndarray]:
         return self._kv[(block, frame)]
 
+    def rows(self, block: int, frame: int, lo: int, hi: int, heads: Optional[List[int]] = None):
+        """Token rows [lo, hi) of one frame, optionally some heads only."""
+        k, v = self._kv[(block, frame)]
+        k, v = k[lo:hi], v[lo:hi]
+        if heads is not None:
+            k, v = k[:, heads], v[:, heads]
+        return k, v
+
 
 class StreamOracle:
     """Plain fp64 streaming attention over the rule-derived visible set."""
@@ -62,27 +70,27 @@ class StreamOracle:
         in visible order: scale frames' patches, window frames' patches, then
         every frame's specials.  ``pending`` supplies frames not yet in the
         history (the current step's)."""
-        def kv_of(f):
+        hs = None if heads is None else list(heads)
+
+        def rows_of(f, lo, hi):
             if pending is not None and f in pending:
-                return pending[f]
-            return self.history.get(block, f)
+                k, v = pending[f]
+                k, v = np.asarray(k[lo:hi], np.float64), np.asarray(v[lo:hi], np.float64)
+                if hs is not None:
+                    k, v = k[:, hs], v[:, hs]
+                return k, v
+            return self.history.rows(block, f, lo, hi, hs)
 
         ks, vs = [], []
         for f in rules.visible_patch_frames(F, self.scale_frames, self.window):
-            k, v = kv_of(f)
-            ks.append(k[:self.P])
-            vs.append(v[:self.P])
+            k, v = rows_of(f, 0, self.P)
+            ks.append(k)
+            vs.append(v)
         for f in rules.visible_special_frames(F):
-            k, v = kv_of(f)
-            ks.append(k[self.P:self.P + self.S])
-            vs.append(v[self.P:self.P + self.S])
-        K = np.concatenate(ks, axis=0)
-        V = np.concatenate(vs, axis=0)
-        if heads is not None:
-            heads = list(heads)
-            K = K[:, heads, :]
-            V = V[:, heads, :]
-        return K, V
+            k, v = rows_of(f, self.P, self.P + self.S)
+            ks.append(k)
+            vs.append(v)
+        return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
 
     def step_outputs(self, block: int, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
                      rows: Optional[np.ndarray] = None, heads: Optional[List[int]] = None):
@@ -97,7 +105,7 @@ class StreamOracle:
             pending[self.F + i] = (np.asarray(k_new[sl], np.float64),
                                    np.asarray(v_new[sl], np.float64))
         hs = list(range(q.shape[1])) if heads is None else list(heads)
-        K, V = self.visible_kv(block, self.F + nf, hs, pending)
+        K, V = self.visible_kv(block, self.F + nf, None if heads is None else hs, pending)
         qq = np.asarray(q, np.float64)[:, hs, :]
         if rows is not None:
             qq = qq[np.asarray(rows)]

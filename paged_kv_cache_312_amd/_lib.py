@@ -1,0 +1,119 @@
+"""ctypes declarations of the C ABI (include/lbm.h and include/lbm_core.h).
+
+Argument marshalling only.  The libraries are built in-tree by
+``paged_kv_cache_312_amd.build``; loading fails loudly when they are missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
+
+LIBDIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib")
+LIB_PATH = os.path.join(LIBDIR, "liblbm.so")
+CORE_PATH = os.path.join(LIBDIR, "liblbm_core.so")
+
+LBM_BF16 = 0
+LBM_F32 = 1
+
+STATUS = {0: "LBM_OK", -1: "LBM_ERR_INVALID_ARG", -2: "LBM_ERR_BAD_STATE",
+          -3: "LBM_ERR_OUT_OF_PAGES", -4: "LBM_ERR_UNSUPPORTED", -5: "LBM_ERR_HIP"}
+
+
+class LbmConfig(ctypes.Structure):
+    _fields_ = [(n, c_int32) for n in (
+        "num_blocks", "num_heads", "head_dim", "patches_per_frame", "special_per_frame",
+        "special_page_size", "scale_frames", "sliding_window", "max_patch_pages",
+        "max_special_pages", "max_frames_per_step", "max_q_tokens", "dtype", "num_splits")]
+
+
+class LbmStats(ctypes.Structure):
+    _fields_ = [(n, c_int32) for n in (
+        "frame_count", "scale_pages", "live_pages", "free_pages", "special_tokens")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class LbmError(RuntimeError):
+    def __init__(self, status: int, func: str, msg: str):
+        super().__init__(f"{func}: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+# name -> (restype, argtypes)
+LBM_FUNCS = {
+    "lbm_query_sizes": (c_int32, [POINTER(LbmConfig), POINTER(c_size_t), POINTER(c_size_t),
+                                  POINTER(c_size_t)]),
+    "lbm_cache_create": (c_int32, [POINTER(LbmConfig), POINTER(c_void_p), POINTER(c_void_p),
+                                   c_void_p, POINTER(c_void_p)]),
+    "lbm_cache_destroy": (None, [c_void_p]),
+    "lbm_cache_reset": (c_int32, [c_void_p]),
+    "lbm_cache_seed_free_lists": (c_int32, [c_void_p, POINTER(c_int32), c_int32,
+                                            POINTER(c_int32), c_int32]),
+    "lbm_append_frame": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p]),
+    "lbm_evict_frames": (c_int32, [c_void_p, POINTER(c_int32), c_int32, POINTER(c_int32)]),
+    "lbm_rollback_last_frame": (c_int32, [c_void_p]),
+    "lbm_plan": (c_int32, [c_void_p, c_int32, c_void_p]),
+    "lbm_run": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p]),
+    "lbm_paged_attention": (c_int32, [POINTER(LbmConfig), c_void_p, c_void_p, c_int32, c_void_p,
+                                      c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p,
+                                      c_void_p]),
+    "lbm_get_stats": (c_int32, [c_void_p, POINTER(LbmStats)]),
+    "lbm_dump_state": (c_int32, [c_void_p, POINTER(c_int32), c_int64, POINTER(c_int64)]),
+    "lbm_get_plan": (c_int32, [c_void_p, POINTER(c_int32), c_int64, POINTER(c_int64)]),
+    "lbm_plan_num_splits": (c_int32, [c_void_p]),
+    "lbm_last_error": (c_char_p, []),
+}
+
+CORE_FUNCS = {
+    "lbmcore_create": (c_int32, [POINTER(LbmConfig), POINTER(c_void_p)]),
+    "lbmcore_destroy": (None, [c_void_p]),
+    "lbmcore_reset": (c_int32, [c_void_p]),
+    "lbmcore_seed_free_lists": (c_int32, [c_void_p, POINTER(c_int32), c_int32, POINTER(c_int32),
+                                          c_int32]),
+    "lbmcore_append": (c_int32, [c_void_p, c_int32]),
+    "lbmcore_write_map": (c_int32, [c_void_p, POINTER(c_int32), c_int64, POINTER(c_int64)]),
+    "lbmcore_evict": (c_int32, [c_void_p, POINTER(c_int32), c_int32, POINTER(c_int32)]),
+    "lbmcore_rollback": (c_int32, [c_void_p]),
+    "lbmcore_plan": (c_int32, [c_void_p, POINTER(c_int32), c_int64, POINTER(c_int64)]),
+    "lbmcore_dump": (c_int32, [c_void_p, POINTER(c_int32), c_int64, POINTER(c_int64)]),
+    "lbmcore_stats": (c_int32, [c_void_p, POINTER(LbmStats)]),
+    "lbmcore_choose_splits": (c_int32, [c_int32] * 7),
+    "lbmcore_last_error": (c_char_p, []),
+}
+
+_libs = {}
+
+
+def _load(path: str, funcs: dict):
+    if path in _libs:
+        return _libs[path]
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{os.path.basename(path)} is not built ({path}); run "
+            "`python -m paged_kv_cache_312_amd.build` first. There is no fallback path.")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in funcs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _libs[path] = lib
+    return lib
+
+
+def lib():
+    """The HIP library (liblbm.so)."""
+    return _load(LIB_PATH, LBM_FUNCS)
+
+
+def core_lib():
+    """The host-only bookkeeping library (liblbm_core.so)."""
+    return _load(CORE_PATH, CORE_FUNCS)
+
+
+def check(status: int, func: str, err_fn) -> None:
+    if status != 0:
+        msg = err_fn()
+        raise LbmError(status, func, msg.decode() if msg else "")

@@ -1,0 +1,466 @@
+// C ABI of liblbm (include/lbm.h): state machine, planner upload, launches.
+//
+// The step protocol follows the pages' per-frame pipeline: append (once per
+// block), evict, plan once at the first block and run in every block ("How
+// the Paged KV Cache Attention Mechanism Enables Long Sequence Inference in
+// LingBot-Map", section "Runtime Flow for Frame Processing"; "How FlashInfer's
+// Paged KV Cache Attention Outperforms SDPA Fallback in Streaming Inference",
+// section "Plan-Run Execution Workflow"), with the deferred-eviction variant in
+// which evict (commit) or rollback follows the runs ("How LingBot-Map Uses KV
+// Caching for Efficient Streaming Inference", section "Flow-Based Keyframe
+// Selection").
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../core/bookkeeping.h"
+#include "kernels.h"
+#include "lbm.h"
+
+namespace lbm {
+
+int32_t attn_occupancy_bf16();
+int32_t attn_occupancy_f32(int32_t head_dim);
+
+int32_t attn_occupancy(int32_t dtype, int32_t head_dim) {
+  return dtype == LBM_BF16 ? attn_occupancy_bf16() : attn_occupancy_f32(head_dim);
+}
+
+void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits) {
+  a->n_tiles = (a->kv_len + kKeysPerTile - 1) / kKeysPerTile;
+  a->tiles_per_split = (a->n_tiles + num_splits - 1) / num_splits;
+  a->num_splits = (a->n_tiles + a->tiles_per_split - 1) / a->tiles_per_split;
+  a->n_qt = (a->Tq + kRowsPerGroup - 1) / kRowsPerGroup;
+  a->rows_pad = a->n_qt * kRowsPerGroup;
+  a->total_items = a->n_qt * a->H * a->num_splits;
+  a->items_per_xcd = (a->total_items + 7) / 8;
+  a->scale_log2 = float(1.4426950408889634 / std::sqrt(double(head_dim)));
+  a->inv_P = 1.0f / float(a->P);
+  a->inv_SPS = 1.0f / float(a->SPS);
+}
+
+static lbm_status kernel_supported(const lbm_config& c) {
+  if (c.dtype == LBM_BF16 && c.head_dim != 64)
+    return fail(LBM_ERR_UNSUPPORTED, "bf16 kernel has head_dim 64 only (got %d)", c.head_dim);
+  if (c.dtype == LBM_F32 && c.head_dim != 64 && c.head_dim != 32)
+    return fail(LBM_ERR_UNSUPPORTED, "fp32 kernel has head_dim 32 or 64 only (got %d)", c.head_dim);
+  return LBM_OK;
+}
+
+static lbm_status hip_fail(hipError_t e, const char* what) {
+  return fail(LBM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace lbm
+
+using namespace lbm;
+
+struct lbm_cache {
+  explicit lbm_cache(const lbm_config& c) : cfg(c), bk(c) {}
+  lbm_config cfg;
+  Bookkeeping bk;
+  std::vector<void*> patch_pools, special_pools;
+  char* workspace = nullptr;
+  WorkspaceLayout ws;
+  int device = 0;
+  int32_t num_cu = 256;
+  int32_t wg_per_cu = 1;
+
+  // open step
+  bool step_open = false;
+  int32_t step_nf = 0;
+  std::vector<uint8_t> appended;
+
+  // current plan
+  bool plan_valid = false;
+  uint64_t plan_epoch = 0;
+  int32_t plan_q = 0;
+  int32_t plan_splits = 0;
+  PlanInfo plan;
+
+  // pinned staging of the table, double-buffered and guarded by events
+  int32_t* staging[2] = {nullptr, nullptr};
+  hipEvent_t staging_ev[2] = {nullptr, nullptr};
+  bool staging_pending[2] = {false, false};
+  int staging_next = 0;
+  size_t staging_bytes = 0;
+};
+
+namespace {
+
+lbm_status check_cache(const lbm_cache* c) {
+  if (!c) return fail(LBM_ERR_INVALID_ARG, "cache is null");
+  return LBM_OK;
+}
+
+lbm_status copy_record(const std::vector<int32_t>& v, int32_t* buf, int64_t cap, int64_t* len) {
+  if (!len) return fail(LBM_ERR_INVALID_ARG, "len is null");
+  if (cap > 0 && !buf) return fail(LBM_ERR_INVALID_ARG, "buf is null");
+  for (int64_t i = 0; i < int64_t(v.size()) && i < cap; ++i) buf[i] = v[size_t(i)];
+  *len = int64_t(v.size());
+  return LBM_OK;
+}
+
+AttnArgs base_args(const lbm_config& c, const void* q, void* out, int32_t nq, const void* ppool,
+                   const void* spool, const int32_t* pids, const int32_t* sids, char* ws_base,
+                   const WorkspaceLayout& ws) {
+  AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.out = out;
+  a.patch_pool = ppool;
+  a.special_pool = spool;
+  a.patch_ids = pids;
+  a.special_ids = sids;
+  a.part_o = reinterpret_cast<float*>(ws_base + ws.part_o_off);
+  a.part_ml = reinterpret_cast<float*>(ws_base + ws.part_ml_off);
+  a.counters = reinterpret_cast<int32_t*>(ws_base + ws.counters_off);
+  a.Tq = nq;
+  a.H = c.num_heads;
+  a.P = c.patches_per_frame;
+  a.SPS = c.special_page_size;
+  return a;
+}
+
+lbm_status launch_attention(const lbm_config& c, AttnArgs* a, int32_t splits, hipStream_t st) {
+  finish_attn_args(a, c.head_dim, splits);
+  const hipError_t e = c.dtype == LBM_BF16 ? launch_attn_bf16(*a, c.head_dim, st)
+                                           : launch_attn_f32(*a, c.head_dim, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return LBM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lbm_last_error(void) { return last_error(); }
+
+lbm_status lbm_query_sizes(const lbm_config* cfg, size_t* patch_pool_bytes,
+                           size_t* special_pool_bytes, size_t* workspace_bytes) {
+  clear_error();
+  if (!cfg) return fail(LBM_ERR_INVALID_ARG, "cfg is null");
+  lbm_status st = validate_config(*cfg);
+  if (st != LBM_OK) return st;
+  const size_t row = size_t(cfg->num_heads) * cfg->head_dim * dtype_size(cfg->dtype);
+  const size_t pp = size_t(cfg->max_patch_pages) * 2 * cfg->patches_per_frame * row;
+  const size_t sp = size_t(cfg->max_special_pages) * 2 * cfg->special_page_size * row;
+  const size_t w = workspace_layout(*cfg).total;
+  if (patch_pool_bytes) *patch_pool_bytes = pp;
+  if (special_pool_bytes) *special_pool_bytes = sp;
+  if (workspace_bytes) *workspace_bytes = w;
+  return LBM_OK;
+}
+
+lbm_status lbm_cache_create(const lbm_config* cfg, void* const* patch_pools,
+                            void* const* special_pools, void* workspace, lbm_cache** out) {
+  clear_error();
+  if (!cfg || !patch_pools || !special_pools || !workspace || !out)
+    return fail(LBM_ERR_INVALID_ARG, "null argument");
+  lbm_status st = validate_config(*cfg);
+  if (st != LBM_OK) return st;
+  if ((st = kernel_supported(*cfg)) != LBM_OK) return st;
+  for (int32_t b = 0; b < cfg->num_blocks; ++b) {
+    if (!patch_pools[b] || !aligned16(patch_pools[b]))
+      return fail(LBM_ERR_INVALID_ARG, "patch pool %d null or not 16-byte aligned", b);
+    if (cfg->max_special_pages > 0 && (!special_pools[b] || !aligned16(special_pools[b])))
+      return fail(LBM_ERR_INVALID_ARG, "special pool %d null or not 16-byte aligned", b);
+  }
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(LBM_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+
+  lbm_cache* c = new (std::nothrow) lbm_cache(*cfg);
+  if (!c) return fail(LBM_ERR_INVALID_ARG, "out of host memory");
+  c->patch_pools.assign(patch_pools, patch_pools + cfg->num_blocks);
+  c->special_pools.assign(special_pools, special_pools + cfg->num_blocks);
+  c->workspace = static_cast<char*>(workspace);
+  c->ws = workspace_layout(*cfg);
+  c->appended.assign(size_t(cfg->num_blocks), 0);
+
+  hipError_t e = hipGetDevice(&c->device);
+  int ncu = 0;
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, c->device);
+  if (e != hipSuccess) {
+    delete c;
+    return hip_fail(e, "device query");
+  }
+  c->num_cu = ncu > 0 ? ncu : 256;
+  c->wg_per_cu = attn_occupancy(cfg->dtype, cfg->head_dim);
+
+  c->staging_bytes = c->ws.special_ids_off - c->ws.patch_ids_off +
+                     sizeof(int32_t) * size_t(std::max(1, cfg->max_special_pages));
+  for (int i = 0; i < 2; ++i) {
+    e = hipHostMalloc(reinterpret_cast<void**>(&c->staging[i]), c->staging_bytes,
+                      hipHostMallocDefault);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->staging_ev[i], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      lbm_cache_destroy(c);
+      return hip_fail(e, "staging allocation");
+    }
+  }
+  // arrival counters start at zero; every launch leaves them at zero
+  e = hipMemset(c->workspace + c->ws.counters_off, 0, sizeof(int32_t) * size_t(c->ws.n_counters));
+  if (e != hipSuccess) {
+    lbm_cache_destroy(c);
+    return hip_fail(e, "workspace clear");
+  }
+  *out = c;
+  return LBM_OK;
+}
+
+void lbm_cache_destroy(lbm_cache* c) {
+  if (!c) return;
+  for (int i = 0; i < 2; ++i) {
+    if (c->staging_ev[i]) {
+      if (c->staging_pending[i]) (void)hipEventSynchronize(c->staging_ev[i]);
+      (void)hipEventDestroy(c->staging_ev[i]);
+    }
+    if (c->staging[i]) (void)hipHostFree(c->staging[i]);
+  }
+  delete c;
+}
+
+lbm_status lbm_cache_reset(lbm_cache* c) {
+  clear_error();
+  lbm_status st = check_cache(c);
+  if (st != LBM_OK) return st;
+  c->bk.reset();
+  c->step_open = false;
+  c->plan_valid = false;
+  return LBM_OK;
+}
+
+lbm_status lbm_cache_seed_free_lists(lbm_cache* c, const int32_t* patch_order, int32_t n_patch,
+                                     const int32_t* special_order, int32_t n_special) {
+  clear_error();
+  lbm_status st = check_cache(c);
+  if (st != LBM_OK) return st;
+  st = c->bk.seed_free_lists(patch_order, n_patch, special_order, n_special);
+  if (st == LBM_OK) {
+    c->step_open = false;
+    c->plan_valid = false;
+  }
+  return st;
+}
+
+lbm_status lbm_append_frame(lbm_cache* c, int32_t block_idx, const void* k, const void* v,
+                            int32_t num_frames, void* hip_stream) {
+  clear_error();
+  lbm_status st = check_cache(c);
+  if (st != LBM_OK) return st;
+  if (block_idx < 0 || block_idx >= c->cfg.num_blocks)
+    return fail(LBM_ERR_INVALID_ARG, "block_idx %d outside 0..%d", block_idx, c->cfg.num_blocks - 1);
+  if (!k || !v || !aligned16(k) || !aligned16(v))
+    return fail(LBM_ERR_INVALID_ARG, "k/v null or not 16-byte aligned");
+  if (num_frames < 1 || num_frames > c->cfg.max_frames_per_step)
+    return fail(LBM_ERR_INVALID_ARG, "num_frames %d outside 1..%d", num_frames,
+                c->cfg.max_frames_per_step);
+  if (block_idx == 0) {
+    if (c->step_open) {
+      for (int32_t b = 0; b < c->cfg.num_blocks; ++b)
+        if (!c->appended[size_t(b)])
+          return fail(LBM_ERR_BAD_STATE, "block %d has not appended the previous step", b);
+    }
+    st = c->bk.reserve(num_frames);
+    if (st != LBM_OK) return st;
+    c->step_open = true;
+    c->step_nf = num_frames;
+    std::fill(c->appended.begin(), c->appended.end(), 0);
+  } else {
+    if (!c->step_open) return fail(LBM_ERR_BAD_STATE, "block %d appends before block 0", block_idx);
+    if (c->appended[size_t(block_idx)])
+      return fail(LBM_ERR_BAD_STATE, "block %d already appended this step", block_idx);
+    if (num_frames != c->step_nf)
+      return fail(LBM_ERR_INVALID_ARG, "block %d appends %d frames, block 0 appended %d",
+                  block_idx, num_frames, c->step_nf);
+  }
+  const WriteMap& wm = c->bk.write_map();
+  AppendArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.k = static_cast<const uint4*>(k);
+  a.v = static_cast<const uint4*>(v);
+  a.patch_pool = static_cast<uint4*>(c->patch_pools[size_t(block_idx)]);
+  a.special_pool = static_cast<uint4*>(c->special_pools[size_t(block_idx)]);
+  a.P = c->cfg.patches_per_frame;
+  a.S = c->cfg.special_per_frame;
+  a.T = a.P + a.S;
+  a.SPS = c->cfg.special_page_size;
+  a.rc = int32_t(size_t(c->cfg.num_heads) * c->cfg.head_dim * dtype_size(c->cfg.dtype) / 16);
+  a.st0 = wm.st0;
+  a.sp_first = wm.sp_first;
+  for (int32_t f = 0; f < wm.nf; ++f) a.patch_pages[f] = wm.patch_pages[f];
+  for (int32_t i = 0; i < wm.n_sp; ++i) a.spages[i] = wm.spages[i];
+  const hipError_t e = launch_append(a, wm.nf, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  c->appended[size_t(block_idx)] = 1;
+  return LBM_OK;
+}
+
+lbm_status lbm_evict_frames(lbm_cache* c, int32_t* evicted_ids, int32_t cap, int32_t* n_evicted) {
+  clear_error();
+  lbm_status st = check_cache(c);
+  if (st != LBM_OK) return st;
+  if (cap > 0 && !evicted_ids) return fail(LBM_ERR_INVALID_ARG, "evicted_ids is null");
+  std::vector<int32_t> ev;
+  st = c->bk.evict(&ev);
+  if (st != LBM_OK) return st;
+  for (size_t i = 0; i < ev.size() && int64_t(i) < cap; ++i) evicted_ids[i] = ev[i];
+  if (n_evicted) *n_evicted = int32_t(ev.size());
+  return LBM_OK;
+}
+
+lbm_status lbm_rollback_last_frame(lbm_cache* c) {
+  clear_error();
+  lbm_status st = check_cache(c);
+  if (st != LBM_OK) return st;
+  st = c->bk.rollback();
+  if (st != LBM_OK) return st;
+  c->step_open = false;
+  return LBM_OK;
+}
+
+lbm_status lbm_plan(lbm_cache* c, int32_t num_q_tokens, void* hip_stream) {
+  clear_error();
+  lbm_status st = check_cache(c);
+  if (st != LBM_OK) return st;
+  if (num_q_tokens < 1 || num_q_tokens > c->cfg.max_q_tokens)
+    return fail(LBM_ERR_INVALID_ARG, "num_q_tokens %d outside 1..%d", num_q_tokens,
+                c->cfg.max_q_tokens);
+  if (c->bk.empty()) return fail(LBM_ERR_BAD_STATE, "plan on an empty cache");
+  const PlanInfo p = c->bk.plan_info();
+  if (p.kv_len < 1) return fail(LBM_ERR_BAD_STATE, "no visible tokens");
+
+  // stage [patch ids | pad | special ids] exactly as laid out in the workspace
+  const int i = c->staging_next;
+  if (c->staging_pending[i]) {
+    const hipError_t e = hipEventSynchronize(c->staging_ev[i]);
+    if (e != hipSuccess) return hip_fail(e, "staging wait");
+    c->staging_pending[i] = false;
+  }
+  std::vector<int32_t> pp;
+  c->bk.visible_patch_pages(&pp);
+  char* stg = reinterpret_cast<char*>(c->staging[i]);
+  std::memcpy(stg, pp.data(), sizeof(int32_t) * pp.size());
+  const size_t sp_off = c->ws.special_ids_off - c->ws.patch_ids_off;
+  const std::vector<int32_t>& sp = c->bk.special_pages();
+  if (!sp.empty()) std::memcpy(stg + sp_off, sp.data(), sizeof(int32_t) * sp.size());
+  const size_t bytes = sp_off + sizeof(int32_t) * sp.size();
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = hipMemcpyAsync(c->workspace + c->ws.patch_ids_off, stg, bytes,
+                                hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipEventRecord(c->staging_ev[i], s);
+  if (e != hipSuccess) return hip_fail(e, "table upload");
+  c->staging_pending[i] = true;
+  c->staging_next = i ^ 1;
+
+  const int32_t cap = split_capacity(c->ws, num_q_tokens);
+  int32_t ns = choose_splits(num_q_tokens, p.kv_len, c->cfg.num_heads, c->num_cu, c->wg_per_cu,
+                             cap, c->cfg.num_splits);
+  if (ns < 1) ns = 1;
+  c->plan = p;
+  c->plan_q = num_q_tokens;
+  c->plan_splits = ns;
+  c->plan_epoch = c->bk.epoch();
+  c->plan_valid = true;
+  return LBM_OK;
+}
+
+int32_t lbm_plan_num_splits(const lbm_cache* c) {
+  return (c && c->plan_valid) ? c->plan_splits : 0;
+}
+
+lbm_status lbm_run(lbm_cache* c, int32_t block_idx, const void* q, void* out,
+                   int32_t num_q_tokens, void* hip_stream) {
+  clear_error();
+  lbm_status st = check_cache(c);
+  if (st != LBM_OK) return st;
+  if (block_idx < 0 || block_idx >= c->cfg.num_blocks)
+    return fail(LBM_ERR_INVALID_ARG, "block_idx %d outside 0..%d", block_idx, c->cfg.num_blocks - 1);
+  if (!q || !out || !aligned16(q) || !aligned16(out))
+    return fail(LBM_ERR_INVALID_ARG, "q/out null or not 16-byte aligned");
+  if (!c->plan_valid) return fail(LBM_ERR_BAD_STATE, "run without a plan");
+  if (c->plan_epoch != c->bk.epoch())
+    return fail(LBM_ERR_BAD_STATE, "plan is stale (append, evict or rollback since)");
+  if (num_q_tokens != c->plan_q)
+    return fail(LBM_ERR_BAD_STATE, "run with %d queries, plan made for %d", num_q_tokens, c->plan_q);
+  if (c->step_open && !c->appended[size_t(block_idx)])
+    return fail(LBM_ERR_BAD_STATE, "block %d has not appended the open step", block_idx);
+  AttnArgs a = base_args(c->cfg, q, out, num_q_tokens, c->patch_pools[size_t(block_idx)],
+                         c->special_pools[size_t(block_idx)],
+                         reinterpret_cast<const int32_t*>(c->workspace + c->ws.patch_ids_off),
+                         reinterpret_cast<const int32_t*>(c->workspace + c->ws.special_ids_off),
+                         c->workspace, c->ws);
+  a.patch_tokens = c->plan.patch_tokens;
+  a.kv_len = c->plan.kv_len;
+  return launch_attention(c->cfg, &a, c->plan_splits, static_cast<hipStream_t>(hip_stream));
+}
+
+lbm_status lbm_paged_attention(const lbm_config* cfg, const void* q, void* out,
+                               int32_t num_q_tokens, const void* patch_pool,
+                               const void* special_pool, const int32_t* patch_ids,
+                               int32_t n_patch_pages, const int32_t* special_ids,
+                               int32_t n_special_tokens, void* workspace, void* hip_stream) {
+  clear_error();
+  if (!cfg) return fail(LBM_ERR_INVALID_ARG, "cfg is null");
+  lbm_status st = validate_config(*cfg);
+  if (st != LBM_OK) return st;
+  if ((st = kernel_supported(*cfg)) != LBM_OK) return st;
+  if (!q || !out || !workspace || !aligned16(q) || !aligned16(out))
+    return fail(LBM_ERR_INVALID_ARG, "q/out/workspace null or misaligned");
+  if (num_q_tokens < 1 || num_q_tokens > cfg->max_q_tokens)
+    return fail(LBM_ERR_INVALID_ARG, "num_q_tokens %d outside 1..%d", num_q_tokens,
+                cfg->max_q_tokens);
+  if (n_patch_pages < 0 || n_special_tokens < 0)
+    return fail(LBM_ERR_INVALID_ARG, "negative table size");
+  if (n_patch_pages > 0 && (!patch_pool || !patch_ids))
+    return fail(LBM_ERR_INVALID_ARG, "patch pool or ids null");
+  if (n_special_tokens > 0 && (!special_pool || !special_ids))
+    return fail(LBM_ERR_INVALID_ARG, "special pool or ids null");
+  const int64_t kv = int64_t(n_patch_pages) * cfg->patches_per_frame + n_special_tokens;
+  if (kv < 1 || kv >= kMaxKvLen) return fail(LBM_ERR_INVALID_ARG, "visible length %lld", (long long)kv);
+  const WorkspaceLayout ws = workspace_layout(*cfg);
+  char* wb = static_cast<char*>(workspace);
+  AttnArgs a = base_args(*cfg, q, out, num_q_tokens, patch_pool, special_pool, patch_ids,
+                         special_ids, wb, ws);
+  a.patch_tokens = n_patch_pages * cfg->patches_per_frame;
+  a.kv_len = int32_t(kv);
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  const int32_t ns = choose_splits(num_q_tokens, a.kv_len, cfg->num_heads, ncu,
+                                   attn_occupancy(cfg->dtype, cfg->head_dim),
+                                   split_capacity(ws, num_q_tokens), cfg->num_splits);
+  return launch_attention(*cfg, &a, ns < 1 ? 1 : ns, static_cast<hipStream_t>(hip_stream));
+}
+
+lbm_status lbm_get_stats(const lbm_cache* c, lbm_stats* out) {
+  clear_error();
+  lbm_status st = check_cache(c);
+  if (st != LBM_OK) return st;
+  if (!out) return fail(LBM_ERR_INVALID_ARG, "out is null");
+  *out = c->bk.stats();
+  return LBM_OK;
+}
+
+lbm_status lbm_dump_state(const lbm_cache* c, int32_t* buf, int64_t cap, int64_t* len) {
+  clear_error();
+  lbm_status st = check_cache(c);
+  if (st != LBM_OK) return st;
+  std::vector<int32_t> v;
+  c->bk.dump(&v);
+  return copy_record(v, buf, cap, len);
+}
+
+lbm_status lbm_get_plan(const lbm_cache* c, int32_t* buf, int64_t cap, int64_t* len) {
+  clear_error();
+  lbm_status st = check_cache(c);
+  if (st != LBM_OK) return st;
+  std::vector<int32_t> v;
+  c->bk.plan_record(&v);
+  return copy_record(v, buf, cap, len);
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Device-side argument blocks and launchers of the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../core/bookkeeping.h"
+
+namespace lbm {
+
+// Append scatter: copy a step's K and V token rows into the reserved patch
+// page of each frame and the packed special slots.
+struct AppendArgs {
+  const uint4* k;          // [nf * T rows][rc chunks]
+  const uint4* v;
+  uint4* patch_pool;       // [pages][2][P][rc]
+  uint4* special_pool;     // [pages][2][SPS][rc]
+  int32_t T, P, S, SPS;
+  int32_t rc;              // 16-byte chunks per token row (H * D * elt / 16)
+  int32_t st0;             // special tokens written before this step
+  int32_t sp_first;        // index of the page holding token st0 in the special page list
+  int32_t patch_pages[kMaxStepFrames];
+  int32_t spages[kMaxStepSpecialPages];
+};
+
+hipError_t launch_append(const AppendArgs& a, int32_t nf, hipStream_t stream);
+
+// Paged attention over a visible table.
+struct AttnArgs {
+  const void* q;              // [Tq][H][D]
+  void* out;                  // [Tq][H][D]
+  const void* patch_pool;     // [pages][2][P][H][D]
+  const void* special_pool;   // [pages][2][SPS][H][D]
+  const int32_t* patch_ids;   // visible patch pages, in table order
+  const int32_t* special_ids; // special pages, in order
+  float* part_o;              // [splits][rows_pad][H][D] unnormalised partial outputs
+  float* part_ml;             // [splits][rows_pad][H][2] (running max, partial sum)
+  int32_t* counters;          // [n_qt * H] arrival counters, zero between launches
+  int32_t Tq, H, P, SPS;
+  int32_t patch_tokens;       // n_patch_pages * P
+  int32_t kv_len;             // patch_tokens + special tokens
+  int32_t n_tiles;            // ceil(kv_len / 64)
+  int32_t num_splits, tiles_per_split;
+  int32_t n_qt;               // ceil(Tq / 128)
+  int32_t rows_pad;           // n_qt * 128
+  int32_t total_items;        // n_qt * H * num_splits
+  int32_t items_per_xcd;      // ceil(total_items / 8)
+  float scale_log2;           // log2(e) / sqrt(D)
+  float inv_P, inv_SPS;       // 1/P, 1/SPS for the position -> page division
+};
+
+// Fill the split/grid fields of `a` for a launch (Tq, kv_len, splits known).
+void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits);
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
+
+// Workgroups of the attention kernel resident per CU (for the planner).
+int32_t attn_occupancy(int32_t dtype, int32_t head_dim);
+
+}  // namespace lbm
