@@ -171,7 +171,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "attn_bf16_d64_kernel", "avg_launch_ms": round(avg_launch_ms, 4),
+                     "kernel": "attn_bf16_d64_kernel (+ merge_kernel): one lbm_run",
+                     "avg_launch_ms": round(avg_launch_ms, 4),
                      "flops_per_launch_avg": flops / n_launch},
         "append": {"bound": "hbm", "achieved": round(append_gbps, 1), "peak": PEAK_HBM_GBPS,
                    "unit": "GB/s", "frac": round(append_gbps / PEAK_HBM_GBPS, 4),

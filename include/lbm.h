@@ -100,8 +100,8 @@ lbm_status lbm_query_sizes(const lbm_config* cfg, size_t* patch_pool_bytes,
 
 /* Create a cache over caller-owned device memory.  patch_pools and
  * special_pools are host arrays of num_blocks device pointers; workspace is a
- * device buffer of the queried size.  Clears the workspace's counters
- * (synchronously).  Patch and special free lists start in ascending id order
+ * device buffer of the queried size.  Patch and special free lists start in
+ * ascending id order
  * ([P4] "Two-Stream Design": pages are allocated from free lists). */
 lbm_status lbm_cache_create(const lbm_config* cfg, void* const* patch_pools,
                             void* const* special_pools, void* workspace, lbm_cache** out);
@@ -170,7 +170,8 @@ lbm_status lbm_plan(lbm_cache* cache, int32_t num_q_tokens, void* hip_stream);
  *   out[i,h,:] = sum_j softmax_j(q[i,h,:] . k[j,h,:] / sqrt(D)) v[j,h,:]
  * over the visible tokens j, read straight from the pages.  No mask inside a
  * step.  q, out: device [num_q_tokens, H, D] in the config dtype (out
- * rounded to nearest even for bf16).  Errors: INVALID_ARG, BAD_STATE (no
+ * rounded to nearest even for bf16).  Enqueues the attention kernel, and a
+ * merge kernel when the plan splits the key range.  Errors: INVALID_ARG, BAD_STATE (no
  * plan, a plan made before the last append/evict/rollback, a different
  * num_q_tokens, or block_idx not yet appended in the open step). */
 lbm_status lbm_run(lbm_cache* cache, int32_t block_idx, const void* q, void* out,
@@ -180,8 +181,9 @@ lbm_status lbm_run(lbm_cache* cache, int32_t block_idx, const void* q, void* out
  * the visible keys are the n_patch_pages patch pages listed in patch_ids
  * (each P tokens) followed by the first n_special_tokens tokens of the
  * special pages listed in special_ids.  Pools, q, out as above; the
- * workspace is one sized by lbm_query_sizes(cfg) and zero-filled before its
- * first use (it returns to zero after every call). */
+ * workspace is a device buffer sized by lbm_query_sizes(cfg) (scratch for the
+ * row table and split partials; no initial contents required).  Enqueues two
+ * to three kernels on hip_stream. */
 lbm_status lbm_paged_attention(const lbm_config* cfg, const void* q, void* out,
                                int32_t num_q_tokens, const void* patch_pool,
                                const void* special_pool, const int32_t* patch_ids,

@@ -169,6 +169,8 @@ class PagedKVCache:
         self.torch = torch
         self.cfg = cfg
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.dtype = torch.bfloat16 if cfg.dtype == LBM_BF16 else torch.float32
         pp_bytes, sp_bytes, ws_bytes = lbm_query_sizes(cfg)
         P, H, D = cfg.patches_per_frame, cfg.num_heads, cfg.head_dim

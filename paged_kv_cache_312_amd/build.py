@@ -24,13 +24,17 @@ LIBDIR = os.path.join(PKG, "lib")
 BUILD = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["hip/api.hip", "hip/append.hip", "hip/attn_bf16.hip", "hip/attn_f32.hip"]
+HIP_SOURCES = ["hip/api.hip", "hip/append.hip", "hip/plan.hip", "hip/attn_bf16.hip",
+               "hip/attn_f32.hip", "hip/merge.hip"]
 CORE_SOURCES = ["core/bookkeeping.cpp"]
 CORE_CAPI = ["core/core_capi.cpp"]
 
 # Packed-FP32 VALU forms stay disabled in device code: hipcc -O3 would form
 # them from float arithmetic by itself.
 HIP_DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# MFMA accumulators in ordinary VGPRs: the softmax works on the score and
+# output accumulators directly, without copies out of the AGPR file.
+HIP_DEVICE_FLAGS += ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def _hipcc() -> str:

@@ -76,8 +76,16 @@ lbm_status validate_config(const lbm_config& c) {
     return fail(LBM_ERR_UNSUPPORTED, "visible key range %lld exceeds %d", (long long)max_kv,
                 kMaxKvLen);
   const int64_t row_elems = int64_t(c.num_heads) * c.head_dim;
-  if ((row_elems * int64_t(dtype_size(c.dtype))) % 16 != 0)
+  const int64_t row_bytes = row_elems * int64_t(dtype_size(c.dtype));
+  if (row_bytes % 16 != 0)
     return fail(LBM_ERR_UNSUPPORTED, "a token row of H*D elements must be a multiple of 16 bytes");
+  // the kernels address a row by a 31-bit byte offset inside its block's pool
+  const int64_t pool_max = std::max(int64_t(c.max_patch_pages) * 2 * c.patches_per_frame,
+                                    int64_t(c.max_special_pages) * 2 * c.special_page_size) *
+                           row_bytes;
+  if (pool_max >= (int64_t(1) << 31))
+    return fail(LBM_ERR_UNSUPPORTED, "one block's pool exceeds 2 GiB (%lld bytes)",
+                (long long)pool_max);
   return LBM_OK;
 }
 
@@ -294,21 +302,28 @@ int32_t choose_splits(int32_t num_q_tokens, int32_t kv_len, int32_t num_heads, i
     return ceil_div(n_tiles, tps);  // no empty split
   };
   if (forced > 0) return normalise(std::min(forced, cap));
+  // Cost model, in tile-times of one workgroup alone on a CU, fitted to the
+  // bf16 kernel on MI355X: k workgroups sharing a CU each take
+  // 1 + 0.58 (k - 1) per tile; every workgroup pays a fixed start/finish cost
+  // of about 12 tiles; splitting adds a merge pass (a launch, ~13 tiles, plus
+  // ~1.8 tiles per split of partials).  Equal workgroups are dispatched in
+  // rounds of num_cu * wg_per_cu; the last, partial round spreads its
+  // workgroups over the CUs.
+  constexpr double kShare = 0.58, kFixed = 12.0, kMergeLaunch = 13.0, kMergePerSplit = 1.8;
   const int64_t units = int64_t(ceil_div(num_q_tokens, kRowsPerGroup)) * num_heads;
   const int64_t slots = int64_t(num_cu) * wg_per_cu;
-  // Critical path in tile-iterations: rounds of workgroups times the tiles one
-  // workgroup walks (plus a fixed start/finish cost), plus the merge reads that
-  // grow with the split count.
-  constexpr double kFixedTiles = 2.0;
-  constexpr double kMergeTilesPerSplit = 0.5;
+  auto per_tile = [&](int64_t k) { return 1.0 + kShare * double(k - 1); };
   int32_t best = 1;
   double best_cost = std::numeric_limits<double>::infinity();
   for (int32_t ns = 1; ns <= cap; ++ns) {
     const int32_t n = normalise(ns);
-    const int32_t tps = ceil_div(n_tiles, n);
+    if (n != ns) continue;
+    const double len = double(ceil_div(n_tiles, n)) + kFixed;
     const int64_t wgs = units * n;
-    const int64_t rounds = (wgs + slots - 1) / slots;
-    const double cost = double(rounds) * (tps + kFixedTiles) + (n > 1 ? kMergeTilesPerSplit * n : 0);
+    const int64_t full = wgs / slots, rest = wgs % slots;
+    double cost = double(full) * len * per_tile(wg_per_cu);
+    if (rest > 0) cost += len * per_tile((rest + num_cu - 1) / num_cu);
+    if (n > 1) cost += kMergeLaunch + kMergePerSplit * n;
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best = n;
@@ -324,9 +339,12 @@ WorkspaceLayout workspace_layout(const lbm_config& c) {
   off = align_up(off + sizeof(int32_t) * size_t(std::max(1, c.scale_frames + c.sliding_window)), 256);
   w.special_ids_off = off;
   off = align_up(off + sizeof(int32_t) * size_t(std::max(1, c.max_special_pages)), 256);
-  w.n_counters = ceil_div(c.max_q_tokens, kRowsPerGroup) * c.num_heads;
-  w.counters_off = off;
-  off = align_up(off + sizeof(int32_t) * size_t(w.n_counters), 256);
+  const int64_t max_kv = int64_t(c.scale_frames + c.sliding_window) * c.patches_per_frame +
+                        int64_t(c.max_special_pages) * c.special_page_size;
+  w.rowtab_len = int32_t((max_kv + kKeysPerTile - 1) / kKeysPerTile * kKeysPerTile);
+  if (w.rowtab_len < kKeysPerTile) w.rowtab_len = kKeysPerTile;
+  w.rowtab_off = off;
+  off = align_up(off + sizeof(uint32_t) * size_t(w.rowtab_len), 256);
   const int32_t rows = ceil_div(std::min(c.max_q_tokens, kSplitRowCap), kRowsPerGroup) * kRowsPerGroup;
   w.split_rows = rows;
   w.part_ml_off = off;

@@ -123,11 +123,11 @@ int32_t choose_splits(int32_t num_q_tokens, int32_t kv_len, int32_t num_heads, i
 struct WorkspaceLayout {
   size_t patch_ids_off = 0;   // int32 [scale_frames + sliding_window]
   size_t special_ids_off = 0; // int32 [max_special_pages]
-  size_t counters_off = 0;    // int32 [n_counters]
+  size_t rowtab_off = 0;      // uint32 [rowtab_len]: per key position, the pool and row
   size_t part_ml_off = 0;     // float [kSplitMax * split_rows * H * 2]
   size_t part_o_off = 0;      // float [kSplitMax * split_rows * H * D]
   size_t total = 0;
-  int32_t n_counters = 0;
+  int32_t rowtab_len = 0;     // longest visible key range, rounded up to whole tiles
   int32_t split_rows = 0;     // partial-result rows per split slot
 };
 WorkspaceLayout workspace_layout(const lbm_config& c);

@@ -36,8 +36,6 @@ void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits) {
   a->total_items = a->n_qt * a->H * a->num_splits;
   a->items_per_xcd = (a->total_items + 7) / 8;
   a->scale_log2 = float(1.4426950408889634 / std::sqrt(double(head_dim)));
-  a->inv_P = 1.0f / float(a->P);
-  a->inv_SPS = 1.0f / float(a->SPS);
 }
 
 static lbm_status kernel_supported(const lbm_config& c) {
@@ -104,8 +102,31 @@ lbm_status copy_record(const std::vector<int32_t>& v, int32_t* buf, int64_t cap,
   return LBM_OK;
 }
 
+// Row table of the visible set described by (patch ids, special ids) into
+// `rowtab`, then the attention launch; both on stream `st`.
+lbm_status launch_rowtab_for(const lbm_config& c, const int32_t* pids, const int32_t* sids,
+                             int32_t patch_tokens, int32_t kv_len, uint32_t* rowtab,
+                             hipStream_t st) {
+  RowtabArgs r;
+  std::memset(&r, 0, sizeof(r));
+  r.patch_ids = pids;
+  r.special_ids = sids;
+  r.rowtab = rowtab;
+  r.P = c.patches_per_frame;
+  r.SPS = c.special_page_size;
+  r.patch_tokens = patch_tokens;
+  r.kv_len = kv_len;
+  r.n_pos = (kv_len + kKeysPerTile - 1) / kKeysPerTile * kKeysPerTile;
+  r.row_bytes = int32_t(size_t(c.num_heads) * c.head_dim * dtype_size(c.dtype));
+  r.inv_P = 1.0f / float(r.P);
+  r.inv_SPS = 1.0f / float(r.SPS);
+  const hipError_t e = launch_rowtab(r, st);
+  if (e != hipSuccess) return hip_fail(e, "row table launch");
+  return LBM_OK;
+}
+
 AttnArgs base_args(const lbm_config& c, const void* q, void* out, int32_t nq, const void* ppool,
-                   const void* spool, const int32_t* pids, const int32_t* sids, char* ws_base,
+                   const void* spool, const uint32_t* rowtab, char* ws_base,
                    const WorkspaceLayout& ws) {
   AttnArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -113,23 +134,26 @@ AttnArgs base_args(const lbm_config& c, const void* q, void* out, int32_t nq, co
   a.out = out;
   a.patch_pool = ppool;
   a.special_pool = spool;
-  a.patch_ids = pids;
-  a.special_ids = sids;
+  a.rowtab = rowtab;
   a.part_o = reinterpret_cast<float*>(ws_base + ws.part_o_off);
   a.part_ml = reinterpret_cast<float*>(ws_base + ws.part_ml_off);
-  a.counters = reinterpret_cast<int32_t*>(ws_base + ws.counters_off);
   a.Tq = nq;
   a.H = c.num_heads;
-  a.P = c.patches_per_frame;
-  a.SPS = c.special_page_size;
+  const int64_t row_bytes = int64_t(c.num_heads) * c.head_dim * int64_t(dtype_size(c.dtype));
+  a.vstride_patch = int32_t(c.patches_per_frame * row_bytes);
+  a.vstride_special = int32_t(c.special_page_size * row_bytes);
   return a;
 }
 
 lbm_status launch_attention(const lbm_config& c, AttnArgs* a, int32_t splits, hipStream_t st) {
   finish_attn_args(a, c.head_dim, splits);
-  const hipError_t e = c.dtype == LBM_BF16 ? launch_attn_bf16(*a, c.head_dim, st)
-                                           : launch_attn_f32(*a, c.head_dim, st);
+  hipError_t e = c.dtype == LBM_BF16 ? launch_attn_bf16(*a, c.head_dim, st)
+                                     : launch_attn_f32(*a, c.head_dim, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (a->num_splits > 1) {
+    e = launch_merge(*a, c.head_dim, c.dtype, st);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
   return LBM_OK;
 }
 
@@ -200,12 +224,6 @@ lbm_status lbm_cache_create(const lbm_config* cfg, void* const* patch_pools,
       lbm_cache_destroy(c);
       return hip_fail(e, "staging allocation");
     }
-  }
-  // arrival counters start at zero; every launch leaves them at zero
-  e = hipMemset(c->workspace + c->ws.counters_off, 0, sizeof(int32_t) * size_t(c->ws.n_counters));
-  if (e != hipSuccess) {
-    lbm_cache_destroy(c);
-    return hip_fail(e, "workspace clear");
   }
   *out = c;
   return LBM_OK;
@@ -355,6 +373,11 @@ lbm_status lbm_plan(lbm_cache* c, int32_t num_q_tokens, void* hip_stream) {
   if (e != hipSuccess) return hip_fail(e, "table upload");
   c->staging_pending[i] = true;
   c->staging_next = i ^ 1;
+  lbm_status rs = launch_rowtab_for(
+      c->cfg, reinterpret_cast<const int32_t*>(c->workspace + c->ws.patch_ids_off),
+      reinterpret_cast<const int32_t*>(c->workspace + c->ws.special_ids_off), p.patch_tokens,
+      p.kv_len, reinterpret_cast<uint32_t*>(c->workspace + c->ws.rowtab_off), s);
+  if (rs != LBM_OK) return rs;
 
   const int32_t cap = split_capacity(c->ws, num_q_tokens);
   int32_t ns = choose_splits(num_q_tokens, p.kv_len, c->cfg.num_heads, c->num_cu, c->wg_per_cu,
@@ -390,10 +413,8 @@ lbm_status lbm_run(lbm_cache* c, int32_t block_idx, const void* q, void* out,
     return fail(LBM_ERR_BAD_STATE, "block %d has not appended the open step", block_idx);
   AttnArgs a = base_args(c->cfg, q, out, num_q_tokens, c->patch_pools[size_t(block_idx)],
                          c->special_pools[size_t(block_idx)],
-                         reinterpret_cast<const int32_t*>(c->workspace + c->ws.patch_ids_off),
-                         reinterpret_cast<const int32_t*>(c->workspace + c->ws.special_ids_off),
+                         reinterpret_cast<const uint32_t*>(c->workspace + c->ws.rowtab_off),
                          c->workspace, c->ws);
-  a.patch_tokens = c->plan.patch_tokens;
   a.kv_len = c->plan.kv_len;
   return launch_attention(c->cfg, &a, c->plan_splits, static_cast<hipStream_t>(hip_stream));
 }
@@ -422,10 +443,16 @@ lbm_status lbm_paged_attention(const lbm_config* cfg, const void* q, void* out,
   const int64_t kv = int64_t(n_patch_pages) * cfg->patches_per_frame + n_special_tokens;
   if (kv < 1 || kv >= kMaxKvLen) return fail(LBM_ERR_INVALID_ARG, "visible length %lld", (long long)kv);
   const WorkspaceLayout ws = workspace_layout(*cfg);
+  if (kv > ws.rowtab_len)
+    return fail(LBM_ERR_INVALID_ARG, "visible length %lld exceeds the config's %d",
+                (long long)kv, ws.rowtab_len);
   char* wb = static_cast<char*>(workspace);
-  AttnArgs a = base_args(*cfg, q, out, num_q_tokens, patch_pool, special_pool, patch_ids,
-                         special_ids, wb, ws);
-  a.patch_tokens = n_patch_pages * cfg->patches_per_frame;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  uint32_t* rowtab = reinterpret_cast<uint32_t*>(wb + ws.rowtab_off);
+  st = launch_rowtab_for(*cfg, patch_ids, special_ids, n_patch_pages * cfg->patches_per_frame,
+                         int32_t(kv), rowtab, stream);
+  if (st != LBM_OK) return st;
+  AttnArgs a = base_args(*cfg, q, out, num_q_tokens, patch_pool, special_pool, rowtab, wb, ws);
   a.kv_len = int32_t(kv);
   int dev = 0, ncu = 256;
   if (hipGetDevice(&dev) == hipSuccess)
@@ -433,7 +460,7 @@ lbm_status lbm_paged_attention(const lbm_config* cfg, const void* q, void* out,
   const int32_t ns = choose_splits(num_q_tokens, a.kv_len, cfg->num_heads, ncu,
                                    attn_occupancy(cfg->dtype, cfg->head_dim),
                                    split_capacity(ws, num_q_tokens), cfg->num_splits);
-  return launch_attention(*cfg, &a, ns < 1 ? 1 : ns, static_cast<hipStream_t>(hip_stream));
+  return launch_attention(*cfg, &a, ns < 1 ? 1 : ns, stream);
 }
 
 lbm_status lbm_get_stats(const lbm_cache* c, lbm_stats* out) {

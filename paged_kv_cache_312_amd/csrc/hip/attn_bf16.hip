@@ -11,41 +11,58 @@
 // Structure (D = 64):
 //  * a workgroup = 4 wavefronts = 128 query rows of one head over one key
 //    range (split); each wavefront owns 32 rows;
-//  * per 64-key tile, K is staged in LDS row-major and V transposed (key-major
-//    columns, keys permuted so each lane's MFMA operand is one 16-byte read),
-//    double-buffered, one barrier per tile; the next tile's global loads are
-//    issued before the current tile's math;
+//  * 64-key tiles of K and V are staged in LDS row-major (K double-buffered, V
+//    triple-buffered), one barrier per tile; global loads are issued one
+//    tile before their LDS store (three before use);
+//  * software pipeline: each step first issues every LDS operand read it
+//    needs (tile t+1's K, tile t's V), then interleaves tile t+1's K Q^T
+//    MFMAs with tile t's exponentials, then runs tile t's P V MFMAs;
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: a lane then holds 16 scores of
 //    one query row, so the row max needs one exchange with lane +-32 and the
 //    row sum none until the end;
-//  * online softmax in fp32 with exp2 and the scale folded in; O is rescaled
-//    only when some row's running max grows;
+//  * per-step row table (one code per key position) gives each K/V row's
+//    address, so the loop does no page arithmetic;
+//  * online softmax in fp32 with exp2 and the scale folded in, against a
+//    running max that is refreshed (and O rescaled) only when a weight would
+//    exceed 256; row sums by bf16 dot products of the rounded weights;
 //  * O^T += V^T P^T on the same MFMA with P taken from registers (no LDS trip),
-//    P rounded to bf16 (round to nearest even);
-//  * with several splits, each writes (O, m, l) partials and the last
-//    workgroup of a (query group, head) merges them.
+//    P rounded to bf16 (round to nearest even); the V operand comes from the
+//    row-major tile through gfx950's LDS transpose reads;
+//  * with several splits, each writes (O, m, l) partials that a separate merge
+//    kernel combines (a kernel boundary orders them: no fences, which on this
+//    chip would write back and invalidate the XCD's L2 that the workgroups
+//    share).
 #include "attn_common.h"
 
 namespace lbm {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int D = 64;
 constexpr int LS = 72;              // LDS row stride in bf16 elements (64 + 8)
-constexpr int TILE = 64 * LS;       // elements of one staged K or V^T tile
+constexpr int TILE = 64 * LS;       // elements of one staged K or V tile
 
-// Column of key k (0..63) inside a V^T row: within each 16-key group, lane
-// half h reads 8 contiguous columns holding keys {4h..4h+3, 8+4h..8+4h+3}.
-__device__ __forceinline__ int vt_col(int k) {
-  const int G = k >> 4, kk = k & 15;
-  const int a = kk >> 3, h = (kk >> 2) & 1, j = kk & 3;
-  return (G << 4) + (h << 3) + (a << 2) + j;
+// 8 keys of V column d for the PV MFMA from a row-major V tile, with two LDS
+// transpose reads: within each 16-lane group, source lane s points at
+// V[k0 + s/4][d0 + 4(s%4)] and output lane i receives V[k0 .. k0+3][d0 + i].
+__device__ __forceinline__ bf16x8 v_operand(const uint16_t* p0, const uint16_t* p1) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+  const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, both);
 }
 
-__global__ __launch_bounds__(kThreads) void attn_bf16_d64_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE];  // [buffer][K | V^T]
+__global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnArgs a) {
+  // K double-buffered, V triple-buffered: while tile t's P V and tile t+1's
+  // K Q^T run, tile t+2 is written.
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[3][TILE];
 
   const int32_t item = work_item(a, blockIdx.x);
   if (item < 0) return;
@@ -77,35 +94,62 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_d64_kernel(const AttnArgs 
   // Loader: thread -> 16-byte chunk lc of keys 2lp and 2lp+1 of a tile.
   const int lc = tid & 7;
   const int lp = tid >> 3;
-  uint4 kreg[2], vreg[2];
-  auto load_tile = [&](int32_t t) {
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      int32_t vd;
-      const uint16_t* kp = key_row<uint16_t>(a, head, t * 64 + 2 * lp + e, HD, D, vd);
-      if (kp) {
-        kreg[e] = *reinterpret_cast<const uint4*>(kp + lc * 8);
-        vreg[e] = *reinterpret_cast<const uint4*>(kp + vd + lc * 8);
-      } else {
-        kreg[e] = make_uint4(0, 0, 0, 0);
-        vreg[e] = make_uint4(0, 0, 0, 0);
-      }
-    }
+  const uint2* tab = reinterpret_cast<const uint2*>(a.rowtab) + lp;
+  const int32_t col_off = (head * D + lc * 8) * 2;
+  struct Stage {
+    uint4 k0, k1, v0, v1;  // K and V rows of keys 2lp and 2lp+1 of one tile
   };
-  const int vcol = vt_col(2 * lp);  // even: keys 2lp, 2lp+1 sit in adjacent columns
-  auto store_tile = [&](int buf) {
-    uint16_t* K = lds[buf][0];
-    uint16_t* Vt = lds[buf][1];
-    *reinterpret_cast<uint4*>(K + (2 * lp) * LS + lc * 8) = kreg[0];
-    *reinterpret_cast<uint4*>(K + (2 * lp + 1) * LS + lc * 8) = kreg[1];
-    const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
-    const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
+  auto gload = [&](uint2 code) __attribute__((always_inline)) {
+    const char *kp0, *vp0, *kp1, *vp1;
+    kv_rows(a, code.x, col_off, kp0, vp0);
+    kv_rows(a, code.y, col_off, kp1, vp1);
+    Stage st;
+    st.k0 = *reinterpret_cast<const uint4*>(kp0);
+    st.v0 = *reinterpret_cast<const uint4*>(vp0);
+    st.k1 = *reinterpret_cast<const uint4*>(kp1);
+    st.v1 = *reinterpret_cast<const uint4*>(vp1);
+    return st;
+  };
+  const int st_off = (2 * lp) * LS + lc * 8;
+  auto lstore = [&](uint16_t* K, uint16_t* V, Stage st) __attribute__((always_inline)) {
+    *reinterpret_cast<uint4*>(K + st_off) = st.k0;
+    *reinterpret_cast<uint4*>(K + st_off + LS) = st.k1;
+    *reinterpret_cast<uint4*>(V + st_off) = st.v0;
+    *reinterpret_cast<uint4*>(V + st_off + LS) = st.v1;
+  };
+
+  // K operand rows of this lane, V transpose-read base of this lane
+  const int k_rd = l32 * LS + hh * 8;
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int v_rd = (4 * (g16 >> 1) + (s16 >> 2)) * LS + (g16 & 1) * 16 + 4 * (s16 & 3);
+
+  // the 8 K operands of a tile (S^T = K Q^T, key blocks kb, column steps ks)
+  auto k_reads = [&](const uint16_t* K, bf16x8* kf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const uint32_t w0 = v0[m >> 1], w1 = v1[m >> 1];
-      const uint32_t packed = (m & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))
-                                      : ((w0 & 0xffffu) | (w1 << 16));
-      *reinterpret_cast<uint32_t*>(Vt + (lc * 8 + m) * LS + vcol) = packed;
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kf[kb * 4 + ks] = *reinterpret_cast<const bf16x8*>(K + k_rd + kb * 32 * LS + ks * 16);
+  };
+  // the 8 V operands of a tile (O^T = V^T P^T, column blocks db, key groups G)
+  auto v_reads = [&](const uint16_t* V, bf16x8* vf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int G = 0; G < 4; ++G) {
+        const uint16_t* p = V + v_rd + (16 * G) * LS + db * 32;
+        vf[db * 4 + G] = v_operand(p, p + 8 * LS);
+      }
+  };
+  // S^T[key][row] of one tile: lane holds row l32 and keys kb*32 + 8i + 4hh + j
+  auto qk = [&](const bf16x8* kf, f32x16* s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb * 4 + ks], qf[ks], s[kb], 0, 0, 0);
     }
   };
 
@@ -114,90 +158,149 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_d64_kernel(const AttnArgs 
   for (int db = 0; db < 2; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  float m_run = -INFINITY;  // running max of this row's raw scores (stale between jumps)
+  float l_run = 0.f;        // this lane's share of the row sum, relative to m_run
   const float c = a.scale_log2;
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  load_tile(t_begin);
-  store_tile(0);
-  __syncthreads();
-
-  for (int32_t t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    const bool has_next = t + 1 < t_end;
-    if (has_next) load_tile(t + 1);
-    const uint16_t* K = lds[buf][0];
-    const uint16_t* Vt = lds[buf][1];
-
-    // scores: S^T[key][row], lane holds row l32 and keys kb*32 + 8i + 4hh + j
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(K + (kb * 32 + l32) * LS + ks * 16 + hh * 8);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
-      }
-    }
-    if ((t + 1) * 64 > a.kv_len) {  // the final tile: keys past the visible set
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int32_t key = t * 64 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-          if (key >= a.kv_len) s[kb][e] = -INFINITY;
-        }
-    }
-
-    float mx = s[0][0];
+  // p = 2^(s*c - m*c) as bf16, grouped as the B operand of the PV MFMA (group
+  // G = 2kb + g holds elements 8g..8g+7 of s[kb]); returns this lane's sum of
+  // the rounded p (exactly the weights the PV product uses).
+  auto exponentiate = [&](const f32x16* s, float mc, bf16x8* pb) __attribute__((always_inline)) {
+    float lt[2] = {0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    if (__ballot(m_new > m_run)) {
-      const float alpha = fast_exp2((m_run - m_new) * c);
+      for (int g = 0; g < 2; ++g) {
+        bf16x8 v;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[u] = static_cast<__bf16>(fast_exp2(fmaf(s[kb][8 * g + u], c, -mc)));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bf16x2 pr = {v[2 * u], v[2 * u + 1]};
+          lt[kb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lt[kb], false);
+        }
+        pb[2 * kb + g] = v;
+      }
+    return lt[0] + lt[1];
+  };
+
+  // prologue: tiles t_begin and t_begin+1 staged, S of t_begin computed, the
+  // global rows of t_begin+2 in flight.  Tile indices past the split's end
+  // are clamped to its last tile: such duplicates land only in buffers that
+  // are no longer read, which keeps the steady-state step free of branches.
+  const int32_t n_t = t_end - t_begin;
+  auto code_of = [&](int32_t i) { return tab[(t_begin + min(i, n_t - 1)) * 32]; };
+  Stage st = gload(code_of(0));
+  lstore(lds_k[0], lds_v[0], st);
+  st = gload(code_of(1));
+  lstore(lds_k[1], lds_v[1], st);
+  uint2 code = code_of(3);
+  __syncthreads();
+  f32x16 s_a[2], s_b[2];
+  {
+    bf16x8 kf[8];
+    k_reads(lds_k[0], kf);
+    qk(kf, s_a);
+  }
+  __syncthreads();  // lds_k[0] is rewritten with tile t_begin+2 in the first step
+  st = gload(code_of(2));
+
+  // Softmax against the running max as it stands; the row max of the tile is
+  // taken only when some weight would leave [0, 256] (the first tile, or a
+  // jump of the max): then O and l are rescaled and the tile redone.  Any max
+  // that is not below the true one gives the same quotient, since numerator
+  // and denominator share it.
+  auto refresh_max = [&](const f32x16* s_cur, bf16x8* pb, float& lt) __attribute__((always_inline)) {
+    if (__ballot(!(lt <= 256.f))) {
+      float mx = s_cur[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s_cur[kb][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2((m_run - m_new) * c);  // 0 on the first tile
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
       m_run = m_new;
+      lt = exponentiate(s_cur, m_run * c, pb);
     }
-    const float mc = m_run * c;
-
-    // P in bf16, grouped as the B operand of the PV MFMA: group G = 2kb + g
-    // holds elements 8g..8g+7 of s[kb].
-    bf16x8 pb[4];
-    float lsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float p = fast_exp2(fmaf(s[kb][8 * g + u], c, -mc));
-          lsum += p;
-          pb[2 * kb + g][u] = static_cast<__bf16>(p);
-        }
-    l_run += lsum;
-
-    // O^T[d][row] += V^T[d][keys] P^T[keys][row]
+  };
+  // O^T[d][row] += V^T[d][keys] P^T[keys][row]
+  auto pv = [&](const bf16x8* vf, const bf16x8* pb) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int G = 0; G < 4; ++G) {
-        const bf16x8 vf =
-            *reinterpret_cast<const bf16x8*>(Vt + (db * 32 + l32) * LS + G * 16 + hh * 8);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[G], o[db], 0, 0, 0);
-      }
+      for (int G = 0; G < 4; ++G)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db * 4 + G], pb[G], o[db], 0, 0, 0);
+  };
 
-    if (has_next) store_tile(buf ^ 1);
+  int vb = 0;  // V buffer of tile t
+  // Steady-state step for tile t = t_begin + i (not the split's last tile):
+  // s_cur holds its scores, s_nxt receives tile t+1's.  Every LDS operand read
+  // of the step goes out first, so their latency hides behind the softmax;
+  // tile t+1's K Q^T MFMAs are interleaved with tile t's exponentials, so the
+  // matrix cores run while the vector ALUs work.
+  auto step = [&](int32_t i, f32x16* s_cur, f32x16* s_nxt) __attribute__((always_inline)) {
+    bf16x8 kf[8], vf[8], pb[4];
+    k_reads(lds_k[(i + 1) & 1], kf);
+    v_reads(lds_v[vb], vf);
+    qk(kf, s_nxt);
+    float lt = exponentiate(s_cur, m_run * c, pb);
+    __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);  // the LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // first exponentials
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // ten VALU
+    }
+    refresh_max(s_cur, pb, lt);
+    l_run += lt;
+    pv(vf, pb);
+    // stage tile t+2 (its K buffer held tile t, its V buffer tile t-1), then
+    // fetch tile t+3 into the staging registers
+    lstore(lds_k[i & 1], lds_v[vb == 0 ? 2 : vb - 1], st);
+    st = gload(code);
+    code = code_of(i + 4);
+    vb = vb == 2 ? 0 : vb + 1;
     __syncthreads();
+  };
+  // The split's last tile: no next tile; keys past the visible set masked.
+  auto last_step = [&](int32_t i, f32x16* s_cur) __attribute__((always_inline)) {
+    const int32_t t = t_begin + i;
+    if ((t + 1) * 64 > a.kv_len) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int32_t key = t * 64 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+          if (key >= a.kv_len) s_cur[kb][e] = -INFINITY;
+        }
+    }
+    bf16x8 vf[8], pb[4];
+    v_reads(lds_v[vb], vf);
+    float lt = exponentiate(s_cur, m_run * c, pb);
+    refresh_max(s_cur, pb, lt);
+    l_run += lt;
+    pv(vf, pb);
+  };
+  // unrolled by two so that the two score buffers swap roles instead of
+  // being copied
+  int32_t i = 0;
+  for (; i + 2 < n_t; i += 2) {
+    step(i, s_a, s_b);
+    step(i + 1, s_b, s_a);
+  }
+  if (n_t - i == 2) {
+    step(i, s_a, s_b);
+    last_step(i + 1, s_b);
+  } else {
+    last_step(i, s_a);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -230,7 +333,6 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_d64_kernel(const AttnArgs 
             make_float4(o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]);
     if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + rh * 2) = make_float2(m_run, l_tot);
   }
-  if (arrive_last(a, qt * a.H + head)) merge_splits<__bf16, D>(a, qt, head);
 }
 
 }  // namespace

@@ -59,19 +59,15 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnArgs a) {
 
   const int lc = tid % CPR;
   const int lk = tid / CPR;
+  const int32_t col_off = (head * D + lc * 4) * 4;
   float4 kreg[PASSES], vreg[PASSES];
   auto load_tile = [&](int32_t t) {
 #pragma unroll
     for (int r = 0; r < PASSES; ++r) {
-      int32_t vd;
-      const float* kp = key_row<float>(a, head, t * 64 + r * KPP + lk, HD, D, vd);
-      if (kp) {
-        kreg[r] = *reinterpret_cast<const float4*>(kp + lc * 4);
-        vreg[r] = *reinterpret_cast<const float4*>(kp + vd + lc * 4);
-      } else {
-        kreg[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-        vreg[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      const char *kp, *vp;
+      kv_rows(a, a.rowtab[t * 64 + r * KPP + lk], col_off, kp, vp);
+      kreg[r] = *reinterpret_cast<const float4*>(kp);
+      vreg[r] = *reinterpret_cast<const float4*>(vp);
     }
   };
   auto store_tile = [&](int buf) {
@@ -200,7 +196,6 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnArgs a) {
             make_float4(o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]);
     if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + rh * 2) = make_float2(m_run, l_tot);
   }
-  if (arrive_last(a, qt * a.H + head)) merge_splits<float, D>(a, qt, head);
 }
 
 }  // namespace

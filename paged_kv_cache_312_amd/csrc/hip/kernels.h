@@ -26,20 +26,37 @@ struct AppendArgs {
 
 hipError_t launch_append(const AppendArgs& a, int32_t nf, hipStream_t stream);
 
+// Row table of a frame step: for each key position j of the visible set, the
+// byte offset of K[j][head 0][0] inside its block's pool, with bit 31 set for
+// the special pool.  Positions past kv_len (up to whole 64-key tiles) repeat
+// position 0, whose scores the attention kernel masks.
+struct RowtabArgs {
+  const int32_t* patch_ids;   // visible patch pages, in table order
+  const int32_t* special_ids; // special pages, in order
+  uint32_t* rowtab;
+  int32_t P, SPS;
+  int32_t patch_tokens;       // n_patch_pages * P
+  int32_t kv_len;
+  int32_t n_pos;              // n_tiles * 64
+  int32_t row_bytes;          // H * D * element size
+  float inv_P, inv_SPS;
+};
+
+hipError_t launch_rowtab(const RowtabArgs& a, hipStream_t stream);
+
 // Paged attention over a visible table.
 struct AttnArgs {
   const void* q;              // [Tq][H][D]
   void* out;                  // [Tq][H][D]
   const void* patch_pool;     // [pages][2][P][H][D]
   const void* special_pool;   // [pages][2][SPS][H][D]
-  const int32_t* patch_ids;   // visible patch pages, in table order
-  const int32_t* special_ids; // special pages, in order
+  const uint32_t* rowtab;     // [n_tiles * 64] row codes (see RowtabArgs)
   float* part_o;              // [splits][rows_pad][H][D] unnormalised partial outputs
   float* part_ml;             // [splits][rows_pad][H][2] (running max, partial sum)
-  int32_t* counters;          // [n_qt * H] arrival counters, zero between launches
-  int32_t Tq, H, P, SPS;
-  int32_t patch_tokens;       // n_patch_pages * P
-  int32_t kv_len;             // patch_tokens + special tokens
+  int32_t Tq, H;
+  int32_t vstride_patch;      // bytes from a K row to its V row: P * H * D * elt
+  int32_t vstride_special;    // SPS * H * D * elt
+  int32_t kv_len;             // visible keys
   int32_t n_tiles;            // ceil(kv_len / 64)
   int32_t num_splits, tiles_per_split;
   int32_t n_qt;               // ceil(Tq / 128)
@@ -47,7 +64,6 @@ struct AttnArgs {
   int32_t total_items;        // n_qt * H * num_splits
   int32_t items_per_xcd;      // ceil(total_items / 8)
   float scale_log2;           // log2(e) / sqrt(D)
-  float inv_P, inv_SPS;       // 1/P, 1/SPS for the position -> page division
 };
 
 // Fill the split/grid fields of `a` for a launch (Tq, kv_len, splits known).
@@ -55,6 +71,10 @@ void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits);
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
+
+// Combine the key-range splits' partials into the output (after an attention
+// launch with num_splits > 1, on the same stream).
+hipError_t launch_merge(const AttnArgs& a, int32_t head_dim, int32_t dtype, hipStream_t stream);
 
 // Workgroups of the attention kernel resident per CU (for the planner).
 int32_t attn_occupancy(int32_t dtype, int32_t head_dim);

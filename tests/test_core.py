@@ -181,8 +181,8 @@ def test_core_rejects_bad_config(bad):
 def test_choose_splits():
     cs = CoreBookkeeping.choose_splits
     # the 24-block ViT-L step: 11 query groups x 16 heads, ~1.55k tiles
-    ns = cs(1375, 99006, 16, 256, 3, 16)
-    assert 2 <= ns <= 16
+    ns = cs(1375, 99006, 16, 256, 2, 16)
+    assert 4 <= ns <= 12
     # the 8-frame first step fills the chip without splitting
     assert cs(11000, 11000, 16, 256, 3, 2) == 1
     # forced counts are honoured and capped; no empty split
