@@ -47,8 +47,9 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the path would shard).", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (independent "
+              "streams would take one cache per GPU; one stream would shard its heads across "
+              "GPUs with replicated page bookkeeping).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
