@@ -45,8 +45,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int D = 64;
-constexpr int LS = 72;              // LDS row stride in bf16 elements (64 + 8)
+constexpr int LS = 64;              // LDS row = one key's 64 columns, 128 bytes
 constexpr int TILE = 64 * LS;       // elements of one staged K or V tile
+
+// Tiles are stored with their 16-byte column chunks XOR-swizzled by row, so
+// that the MFMA operand reads hit 64 distinct banks per LDS cycle: the K
+// operand reads (16 lanes x 16 B of 16 rows) need 8 distinct chunk positions
+// among rows of equal parity; the V transpose reads (32 lanes x 8 B of 4 rows
+// and 4 chunks) need rows r and r+2 on opposite halves of the row.
+__device__ __forceinline__ int k_swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int v_swz(int row) { return ((row >> 1) & 1) * 4; }
 
 // 8 keys of V column d for the PV MFMA from a row-major V tile, with two LDS
 // transpose reads: within each 16-lane group, source lane s points at
@@ -78,26 +86,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
   const int32_t t_begin = split * a.tiles_per_split;
   const int32_t t_end = min(a.n_tiles, t_begin + a.tiles_per_split);
 
-  // Q as the B operand of S^T = K Q^T: row `qrow`, columns 16ks + 8hh .. +7.
+  // Q as the B operand of S^T = K Q^T: row `qrow`, columns 16ks + 8hh .. +7,
+  // pre-multiplied by log2(e)/sqrt(D) (rounded to bf16) so that the MFMA
+  // yields scores in base-2 exponent units.
+  const float c = a.scale_log2;
   const int32_t qrow = qt * 128 + wave * 32 + l32;
   bf16x8 qf[4];
   if (qrow < a.Tq) {
     const bf16x8* qp = reinterpret_cast<const bf16x8*>(
         reinterpret_cast<const uint16_t*>(a.q) + size_t(qrow) * HD + head * D + 8 * hh);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = qp[2 * ks];
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 x = qp[2 * ks];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) qf[ks][u] = static_cast<__bf16>(static_cast<float>(x[u]) * c);
+    }
   } else {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[ks] = bf16x8{};
   }
 
-  // Loader: thread -> 16-byte chunk lc of keys 2lp and 2lp+1 of a tile.
+  // Loader: thread -> 16-byte chunk lc of keys lp and lp+32 of a tile.
   const int lc = tid & 7;
   const int lp = tid >> 3;
-  const uint2* tab = reinterpret_cast<const uint2*>(a.rowtab) + lp;
+  const uint32_t* tab = a.rowtab + lp;
   const int32_t col_off = (head * D + lc * 8) * 2;
   struct Stage {
-    uint4 k0, k1, v0, v1;  // K and V rows of keys 2lp and 2lp+1 of one tile
+    uint4 k0, k1, v0, v1;  // K and V rows of keys lp and lp+32 of one tile
   };
   auto gload = [&](uint2 code) __attribute__((always_inline)) {
     const char *kp0, *vp0, *kp1, *vp1;
@@ -110,18 +125,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
     st.v1 = *reinterpret_cast<const uint4*>(vp1);
     return st;
   };
-  const int st_off = (2 * lp) * LS + lc * 8;
+  // rows lp and lp+32 share their swizzles (32 is a multiple of 16)
+  const int k_st = lp * LS + ((lc ^ k_swz(lp)) * 8);
+  const int v_st = lp * LS + ((lc ^ v_swz(lp)) * 8);
   auto lstore = [&](uint16_t* K, uint16_t* V, Stage st) __attribute__((always_inline)) {
-    *reinterpret_cast<uint4*>(K + st_off) = st.k0;
-    *reinterpret_cast<uint4*>(K + st_off + LS) = st.k1;
-    *reinterpret_cast<uint4*>(V + st_off) = st.v0;
-    *reinterpret_cast<uint4*>(V + st_off + LS) = st.v1;
+    *reinterpret_cast<uint4*>(K + k_st) = st.k0;
+    *reinterpret_cast<uint4*>(K + k_st + 32 * LS) = st.k1;
+    *reinterpret_cast<uint4*>(V + v_st) = st.v0;
+    *reinterpret_cast<uint4*>(V + v_st + 32 * LS) = st.v1;
   };
 
-  // K operand rows of this lane, V transpose-read base of this lane
-  const int k_rd = l32 * LS + hh * 8;
+  // K operand: row kb*32 + l32, chunk 2ks + hh (swizzle depends on l32 only).
+  // V transpose read: within each 16-lane group g, lane s points at row
+  // 4(g/2) + s/4 (+ 16G + 8r) and column db*32 + 16(g%2) + 4(s%4); the row's
+  // swizzle is a lane constant, and the column sits in chunk
+  // db*4 + 2(g%2) + (s%4)/2, at half (s%2).
+  const int k_row = l32 * LS;
+  const int k_x = k_swz(l32);
   const int g16 = lane >> 4, s16 = lane & 15;
-  const int v_rd = (4 * (g16 >> 1) + (s16 >> 2)) * LS + (g16 & 1) * 16 + 4 * (s16 & 3);
+  const int v_row = (4 * (g16 >> 1) + (s16 >> 2)) * LS;
+  const int v_x = v_swz(4 * (g16 >> 1) + (s16 >> 2));
+  const int v_c = 2 * (g16 & 1) + ((s16 & 3) >> 1);
+  const int v_rd0 = v_row + (((0 * 4 + v_c) ^ v_x) * 8) + 4 * (s16 & 1);
+  const int v_rd1 = v_row + (((1 * 4 + v_c) ^ v_x) * 8) + 4 * (s16 & 1);
 
   // the 8 K operands of a tile (S^T = K Q^T, key blocks kb, column steps ks)
   auto k_reads = [&](const uint16_t* K, bf16x8* kf) __attribute__((always_inline)) {
@@ -129,7 +155,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        kf[kb * 4 + ks] = *reinterpret_cast<const bf16x8*>(K + k_rd + kb * 32 * LS + ks * 16);
+        kf[kb * 4 + ks] = *reinterpret_cast<const bf16x8*>(
+            K + k_row + kb * 32 * LS + (((2 * ks + hh) ^ k_x) * 8));
   };
   // the 8 V operands of a tile (O^T = V^T P^T, column blocks db, key groups G)
   auto v_reads = [&](const uint16_t* V, bf16x8* vf) __attribute__((always_inline)) {
@@ -137,18 +164,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int G = 0; G < 4; ++G) {
-        const uint16_t* p = V + v_rd + (16 * G) * LS + db * 32;
+        const uint16_t* p = V + (db == 0 ? v_rd0 : v_rd1) + (16 * G) * LS;
         vf[db * 4 + G] = v_operand(p, p + 8 * LS);
       }
   };
-  // S^T[key][row] of one tile: lane holds row l32 and keys kb*32 + 8i + 4hh + j
-  auto qk = [&](const bf16x8* kf, f32x16* s) __attribute__((always_inline)) {
+  // S^T[key][row] - m of one tile, in base-2 units: lane holds row l32 and
+  // keys kb*32 + 8i + 4hh + j; the accumulator starts from `neg_m` (every
+  // element -m), so the running max is subtracted by the MFMA itself.
+  auto qk = [&](const bf16x8* kf, f32x16* s, const f32x16& neg_m) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb * 4], qf[0], neg_m, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 1; ks < 4; ++ks)
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb * 4 + ks], qf[ks], s[kb], 0, 0, 0);
     }
   };
@@ -158,15 +186,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
   for (int db = 0; db < 2; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
-  float m_run = -INFINITY;  // running max of this row's raw scores (stale between jumps)
-  float l_run = 0.f;        // this lane's share of the row sum, relative to m_run
-  const float c = a.scale_log2;
+  float m_run = 0.f;  // running max of this row's scores in base-2 units (stale between jumps)
+  float l_run = 0.f;  // this lane's share of the row sum, relative to m_run
+  f32x16 neg_m;       // -m_run in every element: the QK accumulator start
+#pragma unroll
+  for (int e = 0; e < 16; ++e) neg_m[e] = 0.f;
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  // p = 2^(s*c - m*c) as bf16, grouped as the B operand of the PV MFMA (group
-  // G = 2kb + g holds elements 8g..8g+7 of s[kb]); returns this lane's sum of
-  // the rounded p (exactly the weights the PV product uses).
-  auto exponentiate = [&](const f32x16* s, float mc, bf16x8* pb) __attribute__((always_inline)) {
+  // p = 2^(s - shift) as bf16 (s already relative to m_run), grouped as the
+  // B operand of the PV MFMA (group G = 2kb + g holds elements 8g..8g+7 of
+  // s[kb]); returns this lane's sum of the rounded p (exactly the weights the
+  // PV product uses).  shift is 0 except after a refresh of the max.
+  auto exponentiate = [&](const f32x16* s, float shift, bf16x8* pb) __attribute__((always_inline)) {
     float lt[2] = {0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -174,8 +205,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
       for (int g = 0; g < 2; ++g) {
         bf16x8 v;
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          v[u] = static_cast<__bf16>(fast_exp2(fmaf(s[kb][8 * g + u], c, -mc)));
+        for (int u = 0; u < 8; ++u) v[u] = static_cast<__bf16>(fast_exp2(s[kb][8 * g + u] - shift));
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const bf16x2 pr = {v[2 * u], v[2 * u + 1]};
@@ -191,7 +221,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
   // are clamped to its last tile: such duplicates land only in buffers that
   // are no longer read, which keeps the steady-state step free of branches.
   const int32_t n_t = t_end - t_begin;
-  auto code_of = [&](int32_t i) { return tab[(t_begin + min(i, n_t - 1)) * 32]; };
+  auto code_of = [&](int32_t i) {
+    const uint32_t* tt = tab + (t_begin + min(i, n_t - 1)) * 64;
+    return make_uint2(tt[0], tt[32]);
+  };
   Stage st = gload(code_of(0));
   lstore(lds_k[0], lds_v[0], st);
   st = gload(code_of(1));
@@ -202,33 +235,46 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
   {
     bf16x8 kf[8];
     k_reads(lds_k[0], kf);
-    qk(kf, s_a);
+    qk(kf, s_a, neg_m);
   }
   __syncthreads();  // lds_k[0] is rewritten with tile t_begin+2 in the first step
   st = gload(code_of(2));
 
-  // Softmax against the running max as it stands; the row max of the tile is
-  // taken only when some weight would leave [0, 256] (the first tile, or a
-  // jump of the max): then O and l are rescaled and the tile redone.  Any max
-  // that is not below the true one gives the same quotient, since numerator
-  // and denominator share it.
-  auto refresh_max = [&](const f32x16* s_cur, bf16x8* pb, float& lt) __attribute__((always_inline)) {
-    if (__ballot(!(lt <= 256.f))) {
+  // Softmax against the running max as it stands (the scores arrive with it
+  // subtracted); the row max of the tile is taken on the split's first tile
+  // and whenever some weight would leave [0, 256] (a jump of the max): then O
+  // and l are rescaled and the tile redone.  Any max that is not below the
+  // true one gives the same quotient, since numerator and denominator share
+  // it; the first tile's refresh makes the largest weight 1, so the row sum
+  // never underflows.
+  // s_nxt (nullable): the next tile's scores, already issued relative to the
+  // old max, are moved to the new one.
+  auto refresh_max = [&](const f32x16* s_cur, f32x16* s_nxt, bf16x8* pb, float& lt, bool first)
+                         __attribute__((always_inline)) {
+    if (__ballot(!(lt <= 256.f)) || first) {
       float mx = s_cur[0][0];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s_cur[kb][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2((m_run - m_new) * c);  // 0 on the first tile
+      mx = fmaxf(mx, __shfl_xor(mx, 32));  // tile max - m_run
+      const float step_up = first ? mx : fmaxf(mx, 0.f);
+      const float alpha = first ? 0.f : fast_exp2(-step_up);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-      m_run = m_new;
-      lt = exponentiate(s_cur, m_run * c, pb);
+      lt = exponentiate(s_cur, step_up, pb);
+      m_run += step_up;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) neg_m[e] = -m_run;
+      if (s_nxt) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s_nxt[kb][e] -= step_up;
+      }
     }
   };
   // O^T[d][row] += V^T[d][keys] P^T[keys][row]
@@ -250,8 +296,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
     bf16x8 kf[8], vf[8], pb[4];
     k_reads(lds_k[(i + 1) & 1], kf);
     v_reads(lds_v[vb], vf);
-    qk(kf, s_nxt);
-    float lt = exponentiate(s_cur, m_run * c, pb);
+    qk(kf, s_nxt, neg_m);
+    float lt = exponentiate(s_cur, 0.f, pb);
     __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);  // the LDS reads
     __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // first exponentials
 #pragma unroll
@@ -259,7 +305,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // ten VALU
     }
-    refresh_max(s_cur, pb, lt);
+    refresh_max(s_cur, s_nxt, pb, lt, i == 0);
     l_run += lt;
     pv(vf, pb);
     // stage tile t+2 (its K buffer held tile t, its V buffer tile t-1), then
@@ -284,8 +330,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
     }
     bf16x8 vf[8], pb[4];
     v_reads(lds_v[vb], vf);
-    float lt = exponentiate(s_cur, m_run * c, pb);
-    refresh_max(s_cur, pb, lt);
+    float lt = exponentiate(s_cur, 0.f, pb);
+    refresh_max(s_cur, nullptr, pb, lt, i == 0);
     l_run += lt;
     pv(vf, pb);
   };

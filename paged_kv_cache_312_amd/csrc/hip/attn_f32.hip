@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnArgs a) {
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<float4*>(po + db * 32 + 8 * i + 4 * hh) =
             make_float4(o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]);
-    if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + rh * 2) = make_float2(m_run, l_tot);
+    if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + rh * 2) = make_float2(m_run * c, l_tot);
   }
 }
 

@@ -52,7 +52,7 @@ struct AttnArgs {
   const void* special_pool;   // [pages][2][SPS][H][D]
   const uint32_t* rowtab;     // [n_tiles * 64] row codes (see RowtabArgs)
   float* part_o;              // [splits][rows_pad][H][D] unnormalised partial outputs
-  float* part_ml;             // [splits][rows_pad][H][2] (running max, partial sum)
+  float* part_ml;             // [splits][rows_pad][H][2] (running max in base-2 units, partial sum)
   int32_t Tq, H;
   int32_t vstride_patch;      // bytes from a K row to its V row: P * H * D * elt
   int32_t vstride_special;    // SPS * H * D * elt

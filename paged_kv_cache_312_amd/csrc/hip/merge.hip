@@ -3,8 +3,9 @@
 // When one (query group, head) is cut into several key ranges, each range
 // leaves an unnormalised partial output O_s with its running max m_s and sum
 // l_s; the result is out = sum_s w_s O_s / sum_s w_s l_s with
-// w_s = 2^((m_s - M) * log2(e)/sqrt(D)), M = max_s m_s -- the usual combination
-// of online-softmax partials (each O_s and l_s is relative to its own m_s).
+// w_s = 2^(m_s - M), M = max_s m_s -- the usual combination of online-softmax
+// partials (each O_s and l_s is relative to its own m_s; maxima are kept in
+// base-2 exponent units, i.e. raw scores times log2(e)/sqrt(D)).
 // Memory-bound: one thread per 4 output columns of one (row, head).
 #include "attn_common.h"
 
@@ -27,7 +28,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
   float den = 0.f;
   for (int32_t s = 0; s < a.num_splits; ++s) {
     const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + (s * split_stride + rh) * 2);
-    const float w = fast_exp2((ml.x - M) * a.scale_log2);
+    const float w = fast_exp2(ml.x - M);
     den += w * ml.y;
     const float4 o = *reinterpret_cast<const float4*>(a.part_o + (s * split_stride + rh) * D + chunk * 4);
     acc.x += w * o.x;
