@@ -11,9 +11,12 @@
 // Structure (D = 64):
 //  * a workgroup = 4 wavefronts = 128 query rows of one head over one key
 //    range (split); each wavefront owns 32 rows;
-//  * 64-key tiles of K and V are staged in LDS row-major (K double-buffered, V
-//    triple-buffered), one barrier per tile; global loads are issued one
-//    tile before their LDS store (three before use);
+//  * 64-key tiles of K and V go from HBM straight into LDS (row-major, global
+//    loads with an LDS destination, no staging registers) through rings of
+//    four stages each, two to three tiles ahead of use; one barrier per tile;
+//  * the row codes that address those loads travel the same way, a ring of
+//    eight tiles' codes in LDS, one stage further ahead, so that waiting for
+//    a code never waits for a newer tile;
 //  * software pipeline: each step first issues every LDS operand read it
 //    needs (tile t+1's K, tile t's V), then interleaves tile t+1's K Q^T
 //    MFMAs with tile t's exponentials, then runs tile t's P V MFMAs;
@@ -47,6 +50,19 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int D = 64;
 constexpr int LS = 64;              // LDS row = one key's 64 columns, 128 bytes
 constexpr int TILE = 64 * LS;       // elements of one staged K or V tile
+constexpr int NST = 4;              // LDS stages of K and of V
+constexpr int NCODE = 2 * NST;      // LDS slots of row codes (64 per tile)
+// Global loads (all with an LDS destination) each wavefront issues per tile:
+// two K, two V, one of row codes.
+constexpr int kLoadsPerStep = 5;
+
+// s_waitcnt with only the vector-memory count constrained (expcnt and
+// lgkmcnt at their maxima); n < 64.
+#define LBM_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+// the same, and every LDS read of this wavefront complete (lgkmcnt 0)
+#define LBM_WAIT_VMCNT_LDS0(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4))
 
 // Tiles are stored with their 16-byte column chunks XOR-swizzled by row, so
 // that the MFMA operand reads hit 64 distinct banks per LDS cycle: the K
@@ -55,6 +71,29 @@ constexpr int TILE = 64 * LS;       // elements of one staged K or V tile
 // and 4 chunks) need rows r and r+2 on opposite halves of the row.
 __device__ __forceinline__ int k_swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int v_swz(int row) { return ((row >> 1) & 1) * 4; }
+
+// Global load with an LDS destination: every lane reads `bytes` from its own
+// address `g`, and the wavefront's data lands contiguously (lane j at byte
+// bytes*j) from LDS address `l` (wavefront-uniform).  Issued as inline asm so
+// that the compiler neither tracks the LDS write nor adds its own waits for
+// it (it cannot tell the ring stages apart and would wait for every such
+// load before each LDS read): the kernel orders these loads itself with
+// vector-memory waits and barriers.  M0 carries the LDS address; no other
+// code in the kernel uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int bytes>
+__device__ __forceinline__ void load_to_lds(const void* g, const void* l) {
+  const uint32_t la = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)l)));
+  if constexpr (bytes == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_nop 0"
+                 :: "s"(la), "v"(g) : "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_nop 0"
+                 :: "s"(la), "v"(g) : "m0");
+}
+#pragma clang diagnostic pop
 
 // 8 keys of V column d for the PV MFMA from a row-major V tile, with two LDS
 // transpose reads: within each 16-lane group, source lane s points at
@@ -67,10 +106,12 @@ __device__ __forceinline__ bf16x8 v_operand(const uint16_t* p0, const uint16_t* 
 }
 
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnArgs a) {
-  // K double-buffered, V triple-buffered: while tile t's P V and tile t+1's
-  // K Q^T run, tile t+2 is written.
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[3][TILE];
+  // Rings indexed by tile position x (x = 0 is the split's first tile): K
+  // and V of tile x in stage x mod NST, its row codes in slot x mod NCODE.
+  // 66 KB, two workgroups per CU.
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[NST][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[NST][TILE];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_code[NCODE][64];
 
   const int32_t item = work_item(a, blockIdx.x);
   if (item < 0) return;
@@ -106,33 +147,52 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
     for (int ks = 0; ks < 4; ++ks) qf[ks] = bf16x8{};
   }
 
-  // Loader: thread -> 16-byte chunk lc of keys lp and lp+32 of a tile.
+  // Loads into LDS: a wavefront instruction fills 1 KB = 8 rows of 128 B,
+  // lane j writing row j/8, 16-byte slot j%8.  Wavefront w fills rows 8w..8w+7
+  // and 32+8w..32+8w+7 of each tile (keys lp and lp+32 for thread tid,
+  // lp = tid/8), and slot lc of a row receives the row's chunk lc ^ swizzle,
+  // which places the tiles in the swizzled layout the operand reads expect.
   const int lc = tid & 7;
   const int lp = tid >> 3;
-  const uint32_t* tab = a.rowtab + lp;
-  const int32_t col_off = (head * D + lc * 8) * 2;
-  struct Stage {
-    uint4 k0, k1, v0, v1;  // K and V rows of keys lp and lp+32 of one tile
+  const int32_t k_col = (head * D + ((lc ^ k_swz(lp)) * 8)) * 2;
+  const int32_t v_col = (head * D + ((lc ^ v_swz(lp)) * 8)) * 2;
+  const int32_t n_t = t_end - t_begin;
+  // tile positions past the split's end are clamped to its last tile: such
+  // loads land only in stages that are never read again, which keeps the
+  // steady-state step free of branches
+  auto tile_at = [&](int32_t x) __attribute__((always_inline)) { return t_begin + min(x, n_t - 1); };
+  auto row_ptr = [&](uint32_t code, bool v) __attribute__((always_inline)) {
+    const bool special = (code >> 31) != 0;
+    const char* base = special ? static_cast<const char*>(a.special_pool)
+                               : static_cast<const char*>(a.patch_pool);
+    const int32_t off = v ? v_col + (special ? a.vstride_special : a.vstride_patch) : k_col;
+    return base + (code & 0x7fffffffu) + off;
   };
-  auto gload = [&](uint2 code) __attribute__((always_inline)) {
-    const char *kp0, *vp0, *kp1, *vp1;
-    kv_rows(a, code.x, col_off, kp0, vp0);
-    kv_rows(a, code.y, col_off, kp1, vp1);
-    Stage st;
-    st.k0 = *reinterpret_cast<const uint4*>(kp0);
-    st.v0 = *reinterpret_cast<const uint4*>(vp0);
-    st.k1 = *reinterpret_cast<const uint4*>(kp1);
-    st.v1 = *reinterpret_cast<const uint4*>(vp1);
-    return st;
+  auto load_k = [&](int32_t stage, uint2 c) __attribute__((always_inline)) {
+    load_to_lds<16>(row_ptr(c.x, false), &lds_k[stage][(8 * wave) * LS]);
+    load_to_lds<16>(row_ptr(c.y, false), &lds_k[stage][(32 + 8 * wave) * LS]);
   };
-  // rows lp and lp+32 share their swizzles (32 is a multiple of 16)
-  const int k_st = lp * LS + ((lc ^ k_swz(lp)) * 8);
-  const int v_st = lp * LS + ((lc ^ v_swz(lp)) * 8);
-  auto lstore = [&](uint16_t* K, uint16_t* V, Stage st) __attribute__((always_inline)) {
-    *reinterpret_cast<uint4*>(K + k_st) = st.k0;
-    *reinterpret_cast<uint4*>(K + k_st + 32 * LS) = st.k1;
-    *reinterpret_cast<uint4*>(V + v_st) = st.v0;
-    *reinterpret_cast<uint4*>(V + v_st + 32 * LS) = st.v1;
+  auto load_v = [&](int32_t stage, uint2 c) __attribute__((always_inline)) {
+    load_to_lds<16>(row_ptr(c.x, true), &lds_v[stage][(8 * wave) * LS]);
+    load_to_lds<16>(row_ptr(c.y, true), &lds_v[stage][(32 + 8 * wave) * LS]);
+  };
+  // all 64 codes of tile position x into their slot (every wavefront loads
+  // the whole slice, so each one waits only for its own loads)
+  auto load_codes = [&](int32_t x) __attribute__((always_inline)) {
+    load_to_lds<4>(a.rowtab + tile_at(x) * 64 + lane, &lds_code[x & (NCODE - 1)][0]);
+  };
+  auto codes_of = [&](int32_t x) __attribute__((always_inline)) {
+    const uint32_t* c = lds_code[x & (NCODE - 1)];
+    return make_uint2(c[lp], c[lp + 32]);
+  };
+  // barrier without a memory fence (the fence would wait for every load
+  // into LDS): each use follows an explicit wait for this wavefront's loads
+  // into LDS that must have landed and for all its LDS reads, since the
+  // compiler may move the consumers of those reads past the barrier
+  auto barrier = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
   // K operand: row kb*32 + l32, chunk 2ks + hh (swizzle depends on l32 only).
@@ -216,29 +276,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
     return lt[0] + lt[1];
   };
 
-  // prologue: tiles t_begin and t_begin+1 staged, S of t_begin computed, the
-  // global rows of t_begin+2 in flight.  Tile indices past the split's end
-  // are clamped to its last tile: such duplicates land only in buffers that
-  // are no longer read, which keeps the steady-state step free of branches.
-  const int32_t n_t = t_end - t_begin;
-  auto code_of = [&](int32_t i) {
-    const uint32_t* tt = tab + (t_begin + min(i, n_t - 1)) * 64;
-    return make_uint2(tt[0], tt[32]);
-  };
-  Stage st = gload(code_of(0));
-  lstore(lds_k[0], lds_v[0], st);
-  st = gload(code_of(1));
-  lstore(lds_k[1], lds_v[1], st);
-  uint2 code = code_of(3);
-  __syncthreads();
+  // Prologue: row codes of tile positions 0 .. 2NST-1; K of positions
+  // 0 .. NST-1 and V of 0 .. NST-2; then S of position 0.  Step i (below)
+  // loads the codes of position i+2NST, reads those of i+NST and loads K of
+  // i+NST with them, and V of i+NST-1 with the codes read one step earlier.
+#pragma unroll
+  for (int x = 0; x < NCODE; ++x) load_codes(x);
+  LBM_WAIT_VMCNT(0);
+  asm volatile("" ::: "memory");  // the code reads below stay after the wait
+  uint2 code_v;
+#pragma unroll
+  for (int x = 0; x < NST; ++x) {
+    code_v = codes_of(x);
+    load_k(x, code_v);
+    if (x < NST - 1) load_v(x, code_v);
+  }
+  // code_v: position NST-1, for the V load of step 0
+  LBM_WAIT_VMCNT_LDS0(0);
+  barrier();
   f32x16 s_a[2], s_b[2];
   {
     bf16x8 kf[8];
     k_reads(lds_k[0], kf);
     qk(kf, s_a, neg_m);
   }
-  __syncthreads();  // lds_k[0] is rewritten with tile t_begin+2 in the first step
-  st = gload(code_of(2));
+  LBM_WAIT_VMCNT_LDS0(63);  // stage 0 of K is reloaded in the first step
+  barrier();
 
   // Softmax against the running max as it stands (the scores arrive with it
   // subtracted); the row max of the tile is taken on the split's first tile
@@ -286,35 +349,44 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db * 4 + G], pb[G], o[db], 0, 0, 0);
   };
 
-  int vb = 0;  // V buffer of tile t
-  // Steady-state step for tile t = t_begin + i (not the split's last tile):
-  // s_cur holds its scores, s_nxt receives tile t+1's.  Every LDS operand read
-  // of the step goes out first, so their latency hides behind the softmax;
-  // tile t+1's K Q^T MFMAs are interleaved with tile t's exponentials, so the
-  // matrix cores run while the vector ALUs work.
+  // Steady-state step for tile position i (not the split's last): s_cur
+  // holds its scores, s_nxt receives position i+1's.  The step's loads into
+  // LDS (to stages last read in the previous step) go out with its LDS
+  // operand reads (position i+1's K, i's V), whose latency hides behind the
+  // softmax; position i+1's K Q^T MFMAs are
+  // interleaved with position i's exponentials, so the matrix cores run
+  // while the vector ALUs work.  At the end each wavefront waits for its
+  // loads of step i-1 (the next step's operands and codes), then the barrier
+  // publishes them to the workgroup.
   auto step = [&](int32_t i, f32x16* s_cur, f32x16* s_nxt) __attribute__((always_inline)) {
+    const uint2 code_k = codes_of(i + NST);
+    load_codes(i + 2 * NST);
     bf16x8 kf[8], vf[8], pb[4];
-    k_reads(lds_k[(i + 1) & 1], kf);
-    v_reads(lds_v[vb], vf);
+    k_reads(lds_k[(i + 1) & (NST - 1)], kf);
+    v_reads(lds_v[i & (NST - 1)], vf);
+    load_k(i & (NST - 1), code_k);
+    load_v((i + NST - 1) & (NST - 1), code_v);
     qk(kf, s_nxt, neg_m);
     float lt = exponentiate(s_cur, 0.f, pb);
-    __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);  // the LDS reads
+    // K operand reads first; the V reads follow the first four MFMAs, whose
+    // K operands are then dead (the two sets are never live together)
+    __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);  // codes + K reads
     __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // first exponentials
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      if (u == 3) __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // V reads
       __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // ten VALU
     }
     refresh_max(s_cur, s_nxt, pb, lt, i == 0);
     l_run += lt;
     pv(vf, pb);
-    // stage tile t+2 (its K buffer held tile t, its V buffer tile t-1), then
-    // fetch tile t+3 into the staging registers
-    lstore(lds_k[i & 1], lds_v[vb == 0 ? 2 : vb - 1], st);
-    st = gload(code);
-    code = code_of(i + 4);
-    vb = vb == 2 ? 0 : vb + 1;
-    __syncthreads();
+    code_v = code_k;
+    // this wavefront's reads of the stages refilled next step are complete
+    // (the compiler may sink their consumers past the barrier), and its
+    // loads of step i-1 have landed
+    LBM_WAIT_VMCNT_LDS0(kLoadsPerStep * (NST - 2));
+    barrier();
   };
   // The split's last tile: no next tile; keys past the visible set masked.
   auto last_step = [&](int32_t i, f32x16* s_cur) __attribute__((always_inline)) {
@@ -329,7 +401,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
         }
     }
     bf16x8 vf[8], pb[4];
-    v_reads(lds_v[vb], vf);
+    v_reads(lds_v[i & (NST - 1)], vf);
     float lt = exponentiate(s_cur, 0.f, pb);
     refresh_max(s_cur, nullptr, pb, lt, i == 0);
     l_run += lt;
@@ -349,6 +421,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
     last_step(i, s_a);
   }
 
+  // loads of clamped positions may still be in flight: the workgroup's LDS
+  // must not be released under them
+  LBM_WAIT_VMCNT(0);
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (a.num_splits == 1) {
     if (qrow < a.Tq) {
