@@ -295,11 +295,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
   LBM_WAIT_VMCNT_LDS0(0);
   barrier();
   f32x16 s_a[2], s_b[2];
-  {
-    bf16x8 kf[8];
-    k_reads(lds_k[0], kf);
-    qk(kf, s_a, neg_m);
-  }
+  bf16x8 kf[8];  // K operands of the next tile position's K Q^T
+  k_reads(lds_k[0], kf);
+  qk(kf, s_a, neg_m);
+  k_reads(lds_k[1], kf);
   LBM_WAIT_VMCNT_LDS0(63);  // stage 0 of K is reloaded in the first step
   barrier();
 
@@ -350,32 +349,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
   };
 
   // Steady-state step for tile position i (not the split's last): s_cur
-  // holds its scores, s_nxt receives position i+1's.  The step's loads into
-  // LDS (to stages last read in the previous step) go out with its LDS
-  // operand reads (position i+1's K, i's V), whose latency hides behind the
-  // softmax; position i+1's K Q^T MFMAs are
-  // interleaved with position i's exponentials, so the matrix cores run
-  // while the vector ALUs work.  At the end each wavefront waits for its
-  // loads of step i-1 (the next step's operands and codes), then the barrier
+  // holds its scores, s_nxt receives position i+1's, whose K operands are
+  // already in registers (read during step i-1), so its K Q^T MFMAs start at
+  // once and are interleaved with position i's exponentials: the matrix
+  // cores run while the vector ALUs work.  The step's loads into LDS (to
+  // stages last read in the previous step) and its V operand reads go out
+  // first; position i+2's K operands are read once the K Q^T MFMAs have
+  // consumed i+1's.  At the end each wavefront waits for its loads of step
+  // i-1 (position i+3's K, the next step's V and codes), then the barrier
   // publishes them to the workgroup.
   auto step = [&](int32_t i, f32x16* s_cur, f32x16* s_nxt) __attribute__((always_inline)) {
     const uint2 code_k = codes_of(i + NST);
     load_codes(i + 2 * NST);
-    bf16x8 kf[8], vf[8], pb[4];
-    k_reads(lds_k[(i + 1) & (NST - 1)], kf);
+    bf16x8 vf[8], pb[4];
     v_reads(lds_v[i & (NST - 1)], vf);
     load_k(i & (NST - 1), code_k);
     load_v((i + NST - 1) & (NST - 1), code_v);
     qk(kf, s_nxt, neg_m);
     float lt = exponentiate(s_cur, 0.f, pb);
-    // K operand reads first; the V reads follow the first four MFMAs, whose
-    // K operands are then dead (the two sets are never live together)
-    __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);  // codes + K reads
+    k_reads(lds_k[(i + 2) & (NST - 1)], kf);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // codes
     __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // first exponentials
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      if (u == 3) __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // V reads
+      if (u == 1) __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // V reads
+      if (u == 7) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // next K reads
       __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // ten VALU
     }
     refresh_max(s_cur, s_nxt, pb, lt, i == 0);
@@ -385,20 +384,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
     // this wavefront's reads of the stages refilled next step are complete
     // (the compiler may sink their consumers past the barrier), and its
     // loads of step i-1 have landed
-    LBM_WAIT_VMCNT_LDS0(kLoadsPerStep * (NST - 2));
+    LBM_WAIT_VMCNT_LDS0(kLoadsPerStep * (NST - 3));
     barrier();
   };
   // The split's last tile: no next tile; keys past the visible set masked.
   auto last_step = [&](int32_t i, f32x16* s_cur) __attribute__((always_inline)) {
     const int32_t t = t_begin + i;
-    if ((t + 1) * 64 > a.kv_len) {
+    {
+      // element e of s_cur[kb] is key t*64 + 4hh + (kb*32 + 8(e/4) + e%4);
+      // applied unconditionally (once per split) to keep one copy of s_cur
+      const int32_t lim = a.kv_len - t * 64 - 4 * hh;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int32_t key = t * 64 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-          if (key >= a.kv_len) s_cur[kb][e] = -INFINITY;
-        }
+        for (int e = 0; e < 16; ++e)
+          s_cur[kb][e] = kb * 32 + 8 * (e >> 2) + (e & 3) >= lim ? -INFINITY : s_cur[kb][e];
     }
     bf16x8 vf[8], pb[4];
     v_reads(lds_v[i & (NST - 1)], vf);
@@ -416,10 +416,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
   }
   if (n_t - i == 2) {
     step(i, s_a, s_b);
-    last_step(i + 1, s_b);
-  } else {
-    last_step(i, s_a);
+    s_a[0] = s_b[0];  // one inlined copy of the last step
+    s_a[1] = s_b[1];
+    ++i;
   }
+  last_step(i, s_a);
 
   // loads of clamped positions may still be in flight: the workgroup's LDS
   // must not be released under them
