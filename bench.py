@@ -41,11 +41,109 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--splits", type=int, default=0, help="force the key-range split count")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the run, stream a 1 GiB buffer through a plain elementwise copy "
+                         "three times (reference for the HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "'bench.py --calibrate-copy' into the traffic record and exit")
     return ap.parse_args()
+
+
+# HBM traffic of one lbm_run, from rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by
+# what the same counters read for a copy of known size.  The record names the
+# sources it was measured on; a changed kernel reports traffic null.
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic__attn_bf16_d64_kernel__vitl_24_block_frame_step.txt")
+KERNEL_SOURCES = ["paged_kv_cache_312_amd/csrc/hip/attn_bf16.hip",
+                  "paged_kv_cache_312_amd/csrc/hip/attn_common.h",
+                  "paged_kv_cache_312_amd/csrc/hip/merge.hip",
+                  "paged_kv_cache_312_amd/csrc/hip/kernels.h"]
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """Bytes per lbm_run from the traffic record, or None if it is missing or
+    was measured on other kernel sources."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.loads(f.read().split("\n", 1)[1])
+    except (OSError, ValueError, IndexError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_lbm_run")
+
+
+def pmc_summary(fetch_dir, write_dir):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the timed attention and
+    merge launches and of the calibration copies -> traffic record."""
+    import csv
+    import glob
+    import statistics
+
+    def load(d, counter):
+        paths = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not paths:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        per = {}
+        for path in paths:
+            for r in csv.DictReader(open(path)):
+                if r["Counter_Name"] != counter:
+                    continue
+                did = int(r["Dispatch_Id"])
+                name = r["Kernel_Name"]
+                per.setdefault(did, [name, 0.0])[1] += float(r["Counter_Value"])
+        return per
+
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = load(d, counter)
+        ids = sorted(per)
+        # steady state only: the two timed steps and the append-timing step
+        # (72 launches at F = 73..75); earlier ones are the first step and
+        # the fill steps, at other shapes
+        attn = [per[i][1] for i in ids if "attn_bf16_d64_kernel" in per[i][0]][-72:]
+        merge = [per[i][1] for i in ids if "merge_kernel" in per[i][0]][-72:]
+        copy = [per[i][1] for i in ids if "elementwise" in per[i][0]][-3:]
+        if not attn or len(copy) < 3:
+            raise SystemExit(f"{counter}: attention or calibration dispatches missing")
+        out[counter] = {"attn_kib": statistics.mean(attn),
+                        "merge_kib": statistics.mean(merge) if merge else 0.0,
+                        "merges_per_attn": len(merge) / len(attn),
+                        "copy_kib": statistics.mean(copy)}
+    f, w = out["FETCH_SIZE"], out["WRITE_SIZE"]
+    f_scale = COPY_BYTES / (f["copy_kib"] * 1024.0)
+    w_scale = COPY_BYTES / (w["copy_kib"] * 1024.0)
+    fetch_b = (f["attn_kib"] + f["merge_kib"] * f["merges_per_attn"]) * 1024.0 * f_scale
+    write_b = (w["attn_kib"] + w["merge_kib"] * w["merges_per_attn"]) * 1024.0 * w_scale
+    rec = {"kernel_source_hash": kernel_source_hash(),
+           "hbm_bytes_per_lbm_run": round(fetch_b + write_b),
+           "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "raw_kib": out, "copy_bytes": COPY_BYTES}
+    os.makedirs(os.path.dirname(TRAFFIC_RECORD), exist_ok=True)
+    with open(TRAFFIC_RECORD, "w") as fh:
+        fh.write("HBM traffic of one lbm_run (attention + merge), 24-block ViT-L step; written by "
+                 "'bench.py --pmc-summary' from two rocprofv3 --pmc runs of 'bench.py --steps 2 "
+                 "--warmup 0 --no-cpu-baseline --calibrate-copy' (FETCH_SIZE, then WRITE_SIZE)\n")
+        fh.write(json.dumps(rec, indent=1) + "\n")
+    print(json.dumps(rec))
 
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path (independent "
               "streams would take one cache per GPU; one stream would shard its heads across "
@@ -171,7 +269,8 @@ def main():
                    "key_splits": splits},
         "roofline": {"bound": "mfma", "achieved": round(achieved_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(),
                      "kernel": "attn_bf16_d64_kernel (+ merge_kernel): one lbm_run",
                      "avg_launch_ms": round(avg_launch_ms, 4),
                      "flops_per_launch_avg": flops / n_launch},
@@ -179,6 +278,14 @@ def main():
                    "unit": "GB/s", "frac": round(append_gbps / PEAK_HBM_GBPS, 4),
                    "avg_launch_ms": round(app_ms, 5), "bytes_per_launch": app_bytes},
     }
+
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, init, sets, F, args.cpu_seconds)
