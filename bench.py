@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+PEAK_FP16_TFLOPS = 2516.6      # MI355X dense fp16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 N_INPUT_SETS = 8
 
@@ -41,6 +42,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--splits", type=int, default=0, help="force the key-range split count")
+    ap.add_argument("--variant-steps", type=int, default=100,
+                    help="timed steps of the same workload in fp16 (reported under 'variants')")
+    ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the run, stream a 1 GiB buffer through a plain elementwise copy "
                          "three times (reference for the HBM byte counters)")
@@ -53,8 +57,8 @@ def parse():
 # HBM traffic of one lbm_run, from rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by
 # what the same counters read for a copy of known size.  The record names the
 # sources it was measured on; a changed kernel reports traffic null.
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic__attn_bf16_d64_kernel__vitl_24_block_frame_step.txt")
-KERNEL_SOURCES = ["paged_kv_cache_312_amd/csrc/hip/attn_bf16.hip",
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic__attn_d64_kernel_bf16__vitl_24_block_frame_step.txt")
+KERNEL_SOURCES = ["paged_kv_cache_312_amd/csrc/hip/attn16.hip",
                   "paged_kv_cache_312_amd/csrc/hip/attn_common.h",
                   "paged_kv_cache_312_amd/csrc/hip/merge.hip",
                   "paged_kv_cache_312_amd/csrc/hip/kernels.h"]
@@ -81,6 +85,12 @@ def recorded_traffic():
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_lbm_run")
+
+
+def bf16_kernel(name: str, base: str) -> bool:
+    """Whether a profiler kernel name (demangled or mangled) is the bf16
+    instance of the template ``base``."""
+    return base in name and ("__bf16" in name or "DF16b" in name)
 
 
 def pmc_summary(fetch_dir, write_dir):
@@ -111,8 +121,8 @@ def pmc_summary(fetch_dir, write_dir):
         # steady state only: the two timed steps and the append-timing step
         # (72 launches at F = 73..75); earlier ones are the first step and
         # the fill steps, at other shapes
-        attn = [per[i][1] for i in ids if "attn_bf16_d64_kernel" in per[i][0]][-72:]
-        merge = [per[i][1] for i in ids if "merge_kernel" in per[i][0]][-72:]
+        attn = [per[i][1] for i in ids if bf16_kernel(per[i][0], "attn_d64_kernel")][-72:]
+        merge = [per[i][1] for i in ids if bf16_kernel(per[i][0], "merge_kernel")][-72:]
         copy = [per[i][1] for i in ids if "elementwise" in per[i][0]][-3:]
         if not attn or len(copy) < 3:
             raise SystemExit(f"{counter}: attention or calibration dispatches missing")
@@ -139,28 +149,20 @@ def pmc_summary(fetch_dir, write_dir):
     print(json.dumps(rec))
 
 
-def main():
-    args = parse()
-    if args.pmc_summary:
-        pmc_summary(*args.pmc_summary)
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: the library has no multi-GPU path (independent "
-              "streams would take one cache per GPU; one stream would shard its heads across "
-              "GPUs with replicated page bookkeeping).", file=sys.stderr)
-        sys.exit(2)
 
-    import numpy as np
+def measure_stream(cfg, dev, steps, warmup, splits_req=0, keep=False):
+    """Stream ``cfg`` through its first step and the window fill, ``warmup``
+    more steps, then time ``steps`` frame steps (all blocks: append, evict and
+    plan once, attention), with HIP events around every lbm_run and every
+    append of one further step.  Returns the figures (and, with ``keep``, the
+    live cache and inputs for the CPU baseline)."""
     import torch
 
     import paged_kv_cache_312_amd as lbm
     import workloads
 
-    cfg = workloads.get_config("vitl_24_block_frame_step")
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     B, H, D, T = cfg.num_blocks, cfg.num_heads, cfg.head_dim, cfg.tokens_per_frame
-    fields = workloads.lbm_config_fields(cfg, num_splits=args.splits)
+    fields = workloads.lbm_config_fields(cfg, num_splits=splits_req)
     cache = lbm.PagedKVCache(lbm.make_config(**fields), dev)
     stream = torch.cuda.current_stream()
 
@@ -168,8 +170,8 @@ def main():
     init = [workloads.gen_step_qkv(cfg, b, 0, cfg.initial_frames, dev) for b in range(B)]
     sets = [[workloads.gen_step_qkv(cfg, b, 1 + i, 1, dev) for b in range(B)]
             for i in range(N_INPUT_SETS)]
-    outs = [torch.empty((T, H, D), dtype=torch.bfloat16, device=dev) for _ in range(B)]
-    out_init = torch.empty((cfg.initial_frames * T, H, D), dtype=torch.bfloat16, device=dev)
+    outs = [torch.empty((T, H, D), dtype=cache.dtype, device=dev) for _ in range(B)]
+    out_init = torch.empty((cfg.initial_frames * T, H, D), dtype=cache.dtype, device=dev)
     torch.cuda.synchronize()
 
     def frame_step(inputs, out_bufs, nq, ev=None):
@@ -192,7 +194,7 @@ def main():
         frame_step(sets[step_idx % N_INPUT_SETS], outs, T)
         F += 1
         step_idx += 1
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         frame_step(sets[step_idx % N_INPUT_SETS], outs, T)
         F += 1
         step_idx += 1
@@ -202,11 +204,11 @@ def main():
     # timed region: K steps; attention launches bracketed by events on the
     # launch stream for the roofline figure
     ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in range(B)] for _ in range(args.steps)]
+           for _ in range(B)] for _ in range(steps)]
     kv_lens = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         frame_step(sets[step_idx % N_INPUT_SETS], outs, T, ev[i])
         F += 1
         step_idx += 1
@@ -218,15 +220,15 @@ def main():
 
     attn_ms = 0.0
     flops = 0.0
-    for i in range(args.steps):
+    for i in range(steps):
         for b in range(B):
             attn_ms += ev[i][b][0].elapsed_time(ev[i][b][1])
         flops += B * 4.0 * T * kv_lens[i] * H * D
-    n_launch = args.steps * B
+    n_launch = steps * B
     avg_launch_ms = attn_ms / n_launch
     achieved_tflops = flops / (attn_ms * 1e-3) / 1e12
-    ms_per_step = elapsed * 1e3 / args.steps
-    fps = args.steps / elapsed
+    ms_per_step = elapsed * 1e3 / steps
+    fps = steps / elapsed
 
     # append bandwidth: one extra timed pass of 24 appends into the live step
     # is not possible without a new reservation, so time the appends of one
@@ -245,8 +247,45 @@ def main():
         cache.run(b, q, outs[b])
     torch.cuda.synchronize()
     app_ms = sum(a.elapsed_time(e) for a, e in e_app) / B
-    app_bytes = 2 * 2 * T * H * D * 2  # K and V rows, read + write, bf16
+    app_bytes = 2 * 2 * T * H * D * cache.dtype.itemsize  # K and V rows, read + write
     append_gbps = app_bytes / (app_ms * 1e-3) / 1e9
+
+    res = {"fps": fps, "ms_per_step": ms_per_step, "tflops": achieved_tflops,
+           "avg_launch_ms": avg_launch_ms, "flops": flops, "n_launch": n_launch,
+           "kv_lens": kv_lens, "splits": splits, "F_first": F_first, "F_last": F,
+           "app_ms": app_ms, "app_bytes": app_bytes, "append_gbps": append_gbps}
+    if keep:
+        res.update(_cache=cache, _init=init, _sets=sets, _F=F)
+    else:
+        cache.close()
+    return res
+
+def main():
+    args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (independent "
+              "streams would take one cache per GPU; one stream would shard its heads across "
+              "GPUs with replicated page bookkeeping).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+
+    cfg = workloads.get_config("vitl_24_block_frame_step")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    m = measure_stream(cfg, dev, args.steps, args.warmup, args.splits, keep=True)
+    B, H, D, T = cfg.num_blocks, cfg.num_heads, cfg.head_dim, cfg.tokens_per_frame
+    cache, init, sets, F = m.pop("_cache"), m.pop("_init"), m.pop("_sets"), m.pop("_F")
+    kv_lens, splits = m["kv_lens"], m["splits"]
+    fps, ms_per_step, achieved_tflops = m["fps"], m["ms_per_step"], m["tflops"]
+    avg_launch_ms, flops, n_launch = m["avg_launch_ms"], m["flops"], m["n_launch"]
+    F_first = m["F_first"]
+    app_ms, app_bytes, append_gbps = m["app_ms"], m["app_bytes"], m["append_gbps"]
 
     result = {
         "metric": "frames/sec per 24-block step at window 64 + attention MFMA util vs bf16 peak",
@@ -271,13 +310,26 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(),
-                     "kernel": "attn_bf16_d64_kernel (+ merge_kernel): one lbm_run",
+                     "kernel": "attn_d64_kernel<__bf16> (+ merge_kernel): one lbm_run",
                      "avg_launch_ms": round(avg_launch_ms, 4),
                      "flops_per_launch_avg": flops / n_launch},
         "append": {"bound": "hbm", "achieved": round(append_gbps, 1), "peak": PEAK_HBM_GBPS,
                    "unit": "GB/s", "frac": round(append_gbps / PEAK_HBM_GBPS, 4),
                    "avg_launch_ms": round(app_ms, 5), "bytes_per_launch": app_bytes},
     }
+
+    cache.close()
+    if not args.no_variants:
+        # the same 24-block stream with fp16 storage and MFMA (the pages' other
+        # 16-bit type); a shorter timed run after the same fill
+        v = measure_stream(cfg.replace(dtype="f16"), dev, args.variant_steps, args.warmup,
+                           args.splits)
+        result["variants"] = {"fp16": {
+            "value": round(v["fps"], 3), "unit": "frames/s", "steps": args.variant_steps,
+            "timed_frames": [v["F_first"], v["F_last"]],
+            "attention_tflops": round(v["tflops"], 2),
+            "frac": round(v["tflops"] / PEAK_FP16_TFLOPS, 4), "peak": PEAK_FP16_TFLOPS,
+            "avg_launch_ms": round(v["avg_launch_ms"], 4), "key_splits": v["splits"]}}
 
     if args.calibrate_copy:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -289,7 +341,6 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, init, sets, F, args.cpu_seconds)
-    cache.close()
     print(json.dumps(result), flush=True)
 
 

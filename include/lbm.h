@@ -49,7 +49,10 @@ extern "C" {
 
 typedef enum lbm_dtype {
   LBM_BF16 = 0, /* bf16 storage, bf16 MFMA products, fp32 softmax and accumulation */
-  LBM_F32 = 1   /* fp32 throughout (the force_fp32 path, [P2] "Memory Efficiency Analysis") */
+  LBM_F32 = 1,  /* fp32 throughout (the force_fp32 path, [P2] "Memory Efficiency Analysis") */
+  LBM_F16 = 2   /* fp16 storage, fp16 MFMA products, fp32 softmax and accumulation (the
+                   pages' kernels run natively on fp16 or bf16: [P4] "Precision and Hardware
+                   Utilization") */
 } lbm_dtype;
 
 typedef enum lbm_status {

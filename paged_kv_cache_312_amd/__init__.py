@@ -12,10 +12,10 @@ import ctypes
 from ctypes import byref, c_int32, c_int64, c_size_t, c_void_p
 from typing import List, Optional, Sequence, Tuple
 
-from ._lib import (LBM_BF16, LBM_F32, LbmConfig, LbmError, LbmStats, check, core_lib, lib)
+from ._lib import (LBM_BF16, LBM_F16, LBM_F32, LbmConfig, LbmError, LbmStats, check, core_lib, lib)
 
 __all__ = [
-    "LBM_BF16", "LBM_F32", "LbmConfig", "LbmError", "LbmStats", "make_config",
+    "LBM_BF16", "LBM_F16", "LBM_F32", "LbmConfig", "LbmError", "LbmStats", "make_config",
     "lbm_query_sizes", "lbm_cache_create", "lbm_cache_destroy", "lbm_cache_reset",
     "lbm_cache_seed_free_lists", "lbm_append_frame", "lbm_evict_frames",
     "lbm_rollback_last_frame", "lbm_plan", "lbm_run", "lbm_paged_attention", "lbm_get_stats",
@@ -171,7 +171,8 @@ class PagedKVCache:
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
-        self.dtype = torch.bfloat16 if cfg.dtype == LBM_BF16 else torch.float32
+        self.dtype = {LBM_BF16: torch.bfloat16, LBM_F16: torch.float16,
+                      LBM_F32: torch.float32}[cfg.dtype]
         pp_bytes, sp_bytes, ws_bytes = lbm_query_sizes(cfg)
         P, H, D = cfg.patches_per_frame, cfg.num_heads, cfg.head_dim
         self.patch_pools = torch.empty((cfg.num_blocks, cfg.max_patch_pages, 2, P, H, D),

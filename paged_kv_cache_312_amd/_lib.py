@@ -15,6 +15,7 @@ CORE_PATH = os.path.join(LIBDIR, "liblbm_core.so")
 
 LBM_BF16 = 0
 LBM_F32 = 1
+LBM_F16 = 2
 
 STATUS = {0: "LBM_OK", -1: "LBM_ERR_INVALID_ARG", -2: "LBM_ERR_BAD_STATE",
           -3: "LBM_ERR_OUT_OF_PAGES", -4: "LBM_ERR_UNSUPPORTED", -5: "LBM_ERR_HIP"}

@@ -24,7 +24,7 @@ LIBDIR = os.path.join(PKG, "lib")
 BUILD = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["hip/api.hip", "hip/append.hip", "hip/plan.hip", "hip/attn_bf16.hip",
+HIP_SOURCES = ["hip/api.hip", "hip/append.hip", "hip/plan.hip", "hip/attn16.hip",
                "hip/attn_f32.hip", "hip/merge.hip"]
 CORE_SOURCES = ["core/bookkeeping.cpp"]
 CORE_CAPI = ["core/core_capi.cpp"]

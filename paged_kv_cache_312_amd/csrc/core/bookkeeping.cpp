@@ -37,7 +37,7 @@ lbm_status fail(lbm_status st, const char* fmt, ...) {
 void clear_error() { g_error.clear(); }
 const char* last_error() { return g_error.c_str(); }
 
-size_t dtype_size(int32_t dtype) { return dtype == LBM_BF16 ? 2 : 4; }
+size_t dtype_size(int32_t dtype) { return dtype == LBM_F32 ? 4 : 2; }
 
 lbm_status validate_config(const lbm_config& c) {
   if (c.num_blocks < 1) return fail(LBM_ERR_INVALID_ARG, "num_blocks %d < 1", c.num_blocks);
@@ -59,7 +59,7 @@ lbm_status validate_config(const lbm_config& c) {
     return fail(LBM_ERR_INVALID_ARG, "max_frames_per_step %d outside 1..%d",
                 c.max_frames_per_step, kMaxStepFrames);
   if (c.max_q_tokens < 1) return fail(LBM_ERR_INVALID_ARG, "max_q_tokens %d < 1", c.max_q_tokens);
-  if (c.dtype != LBM_BF16 && c.dtype != LBM_F32)
+  if (c.dtype != LBM_BF16 && c.dtype != LBM_F32 && c.dtype != LBM_F16)
     return fail(LBM_ERR_INVALID_ARG, "dtype %d", c.dtype);
   if (c.num_splits < 0) return fail(LBM_ERR_INVALID_ARG, "num_splits %d < 0", c.num_splits);
   // special pages one append can touch must fit the kernel argument block

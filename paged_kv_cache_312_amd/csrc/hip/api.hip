@@ -20,11 +20,11 @@
 
 namespace lbm {
 
-int32_t attn_occupancy_bf16();
+int32_t attn_occupancy16();
 int32_t attn_occupancy_f32(int32_t head_dim);
 
 int32_t attn_occupancy(int32_t dtype, int32_t head_dim) {
-  return dtype == LBM_BF16 ? attn_occupancy_bf16() : attn_occupancy_f32(head_dim);
+  return dtype == LBM_F32 ? attn_occupancy_f32(head_dim) : attn_occupancy16();
 }
 
 void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits) {
@@ -39,8 +39,8 @@ void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits) {
 }
 
 static lbm_status kernel_supported(const lbm_config& c) {
-  if (c.dtype == LBM_BF16 && c.head_dim != 64)
-    return fail(LBM_ERR_UNSUPPORTED, "bf16 kernel has head_dim 64 only (got %d)", c.head_dim);
+  if (c.dtype != LBM_F32 && c.head_dim != 64)
+    return fail(LBM_ERR_UNSUPPORTED, "16-bit kernels have head_dim 64 only (got %d)", c.head_dim);
   if (c.dtype == LBM_F32 && c.head_dim != 64 && c.head_dim != 32)
     return fail(LBM_ERR_UNSUPPORTED, "fp32 kernel has head_dim 32 or 64 only (got %d)", c.head_dim);
   return LBM_OK;
@@ -147,8 +147,8 @@ AttnArgs base_args(const lbm_config& c, const void* q, void* out, int32_t nq, co
 
 lbm_status launch_attention(const lbm_config& c, AttnArgs* a, int32_t splits, hipStream_t st) {
   finish_attn_args(a, c.head_dim, splits);
-  hipError_t e = c.dtype == LBM_BF16 ? launch_attn_bf16(*a, c.head_dim, st)
-                                     : launch_attn_f32(*a, c.head_dim, st);
+  hipError_t e = c.dtype == LBM_F32 ? launch_attn_f32(*a, c.head_dim, st)
+                                    : launch_attn16(*a, c.head_dim, c.dtype == LBM_F16, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   if (a->num_splits > 1) {
     e = launch_merge(*a, c.head_dim, c.dtype, st);

@@ -1,4 +1,4 @@
-// Paged flash attention, bf16 inputs, MFMA on gfx950 (CDNA4).
+// Paged flash attention, 16-bit inputs (bf16 or fp16), MFMA on gfx950 (CDNA4).
 //
 // Computes, for every query row i and head h of a frame step, softmax over
 // the visible keys of q.k / sqrt(D) applied to v, reading K/V straight from
@@ -6,7 +6,12 @@
 // Attention Enables ~20 FPS Streaming Inference in LingBot-Map", section
 // "FlashInfer Paged-Kernel Integration"; "How the Paged KV Cache Attention
 // Mechanism Enables Long Sequence Inference in LingBot-Map", section
-// "FlashInfer Kernel Execution").  No mask inside a step.
+// "FlashInfer Kernel Execution").  No mask inside a step.  The pages run the
+// kernel natively on either 16-bit type ("How FlashInfer's Paged KV Cache
+// Attention Outperforms SDPA Fallback in Streaming Inference", section
+// "Precision and Hardware Utilization"): one template, instantiated for bf16
+// and fp16, which differ only in the MFMA, the dot product of the row sums
+// and the conversions.
 //
 // Structure (D = 64):
 //  * a workgroup = 4 wavefronts = 128 query rows of one head over one key
@@ -20,16 +25,16 @@
 //  * software pipeline: each step first issues every LDS operand read it
 //    needs (tile t+1's K, tile t's V), then interleaves tile t+1's K Q^T
 //    MFMAs with tile t's exponentials, then runs tile t's P V MFMAs;
-//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: a lane then holds 16 scores of
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_{bf16,f16}: a lane then holds 16 scores of
 //    one query row, so the row max needs one exchange with lane +-32 and the
 //    row sum none until the end;
 //  * per-step row table (one code per key position) gives each K/V row's
 //    address, so the loop does no page arithmetic;
 //  * online softmax in fp32 with exp2 and the scale folded in, against a
 //    running max that is refreshed (and O rescaled) only when a weight would
-//    exceed 256; row sums by bf16 dot products of the rounded weights;
+//    exceed 256; row sums by 16-bit dot products of the rounded weights;
 //  * O^T += V^T P^T on the same MFMA with P taken from registers (no LDS trip),
-//    P rounded to bf16 (round to nearest even); the V operand comes from the
+//    P rounded to the input type (round to nearest even); the V operand comes from the
 //    row-major tile through gfx950's LDS transpose reads;
 //  * with several splits, each writes (O, m, l) partials that a separate merge
 //    kernel combines (a kernel boundary orders them: no fences, which on this
@@ -40,12 +45,34 @@
 namespace lbm {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// The element type's MFMA (32x32x16, fp32 accumulate) and pair dot product
+// (fp32 accumulate).
+template <typename T> struct Elt;
+template <> struct Elt<__bf16> {
+  typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float dot2(v2 a, v2 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+  }
+};
+template <> struct Elt<_Float16> {
+  typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float dot2(v2 a, v2 b, float c) {
+    return __builtin_amdgcn_fdot2(a, b, c, false);
+  }
+};
 
 constexpr int D = 64;
 constexpr int LS = 64;              // LDS row = one key's 64 columns, 128 bytes
@@ -98,14 +125,19 @@ __device__ __forceinline__ void load_to_lds(const void* g, const void* l) {
 // 8 keys of V column d for the PV MFMA from a row-major V tile, with two LDS
 // transpose reads: within each 16-lane group, source lane s points at
 // V[k0 + s/4][d0 + 4(s%4)] and output lane i receives V[k0 .. k0+3][d0 + i].
-__device__ __forceinline__ bf16x8 v_operand(const uint16_t* p0, const uint16_t* p1) {
+template <typename V8>
+__device__ __forceinline__ V8 v_operand(const uint16_t* p0, const uint16_t* p1) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
   const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, both);
+  return __builtin_bit_cast(V8, both);
 }
 
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnArgs a) {
+// one kernel per element type: attn_d64_kernel<__bf16> and attn_d64_kernel<_Float16>
+template <typename T>
+__global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const AttnArgs a) {
+  typedef typename Elt<T>::v8 h8;
+  typedef typename Elt<T>::v2 h2;
   // Rings indexed by tile position x (x = 0 is the split's first tile): K
   // and V of tile x in stage x mod NST, its row codes in slot x mod NCODE.
   // 66 KB, two workgroups per CU.
@@ -128,23 +160,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
   const int32_t t_end = min(a.n_tiles, t_begin + a.tiles_per_split);
 
   // Q as the B operand of S^T = K Q^T: row `qrow`, columns 16ks + 8hh .. +7,
-  // pre-multiplied by log2(e)/sqrt(D) (rounded to bf16) so that the MFMA
+  // pre-multiplied by log2(e)/sqrt(D) (rounded to T) so that the MFMA
   // yields scores in base-2 exponent units.
   const float c = a.scale_log2;
   const int32_t qrow = qt * 128 + wave * 32 + l32;
-  bf16x8 qf[4];
+  h8 qf[4];
   if (qrow < a.Tq) {
-    const bf16x8* qp = reinterpret_cast<const bf16x8*>(
+    const h8* qp = reinterpret_cast<const h8*>(
         reinterpret_cast<const uint16_t*>(a.q) + size_t(qrow) * HD + head * D + 8 * hh);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 x = qp[2 * ks];
+      const h8 x = qp[2 * ks];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) qf[ks][u] = static_cast<__bf16>(static_cast<float>(x[u]) * c);
+      for (int u = 0; u < 8; ++u) qf[ks][u] = static_cast<T>(static_cast<float>(x[u]) * c);
     }
   } else {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = bf16x8{};
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = h8{};
   }
 
   // Loads into LDS: a wavefront instruction fills 1 KB = 8 rows of 128 B,
@@ -210,34 +242,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
   const int v_rd1 = v_row + (((1 * 4 + v_c) ^ v_x) * 8) + 4 * (s16 & 1);
 
   // the 8 K operands of a tile (S^T = K Q^T, key blocks kb, column steps ks)
-  auto k_reads = [&](const uint16_t* K, bf16x8* kf) __attribute__((always_inline)) {
+  auto k_reads = [&](const uint16_t* K, h8* kf) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        kf[kb * 4 + ks] = *reinterpret_cast<const bf16x8*>(
+        kf[kb * 4 + ks] = *reinterpret_cast<const h8*>(
             K + k_row + kb * 32 * LS + (((2 * ks + hh) ^ k_x) * 8));
   };
   // the 8 V operands of a tile (O^T = V^T P^T, column blocks db, key groups G)
-  auto v_reads = [&](const uint16_t* V, bf16x8* vf) __attribute__((always_inline)) {
+  auto v_reads = [&](const uint16_t* V, h8* vf) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int G = 0; G < 4; ++G) {
         const uint16_t* p = V + (db == 0 ? v_rd0 : v_rd1) + (16 * G) * LS;
-        vf[db * 4 + G] = v_operand(p, p + 8 * LS);
+        vf[db * 4 + G] = v_operand<h8>(p, p + 8 * LS);
       }
   };
   // S^T[key][row] - m of one tile, in base-2 units: lane holds row l32 and
   // keys kb*32 + 8i + 4hh + j; the accumulator starts from `neg_m` (every
   // element -m), so the running max is subtracted by the MFMA itself.
-  auto qk = [&](const bf16x8* kf, f32x16* s, const f32x16& neg_m) __attribute__((always_inline)) {
+  auto qk = [&](const h8* kf, f32x16* s, const f32x16& neg_m) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb * 4], qf[0], neg_m, 0, 0, 0);
+      s[kb] = Elt<T>::mfma(kf[kb * 4], qf[0], neg_m);
 #pragma unroll
       for (int ks = 1; ks < 4; ++ks)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb * 4 + ks], qf[ks], s[kb], 0, 0, 0);
+        s[kb] = Elt<T>::mfma(kf[kb * 4 + ks], qf[ks], s[kb]);
     }
   };
 
@@ -251,25 +283,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
   f32x16 neg_m;       // -m_run in every element: the QK accumulator start
 #pragma unroll
   for (int e = 0; e < 16; ++e) neg_m[e] = 0.f;
-  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  const h2 ones = {static_cast<T>(1.0f), static_cast<T>(1.0f)};
 
-  // p = 2^(s - shift) as bf16 (s already relative to m_run), grouped as the
+  // p = 2^(s - shift) in T (s already relative to m_run), grouped as the
   // B operand of the PV MFMA (group G = 2kb + g holds elements 8g..8g+7 of
   // s[kb]); returns this lane's sum of the rounded p (exactly the weights the
   // PV product uses).  shift is 0 except after a refresh of the max.
-  auto exponentiate = [&](const f32x16* s, float shift, bf16x8* pb) __attribute__((always_inline)) {
+  auto exponentiate = [&](const f32x16* s, float shift, h8* pb) __attribute__((always_inline)) {
     float lt[2] = {0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        bf16x8 v;
+        h8 v;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = static_cast<__bf16>(fast_exp2(s[kb][8 * g + u] - shift));
+        for (int u = 0; u < 8; ++u) v[u] = static_cast<T>(fast_exp2(s[kb][8 * g + u] - shift));
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const bf16x2 pr = {v[2 * u], v[2 * u + 1]};
-          lt[kb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lt[kb], false);
+          const h2 pr = {v[2 * u], v[2 * u + 1]};
+          lt[kb] = Elt<T>::dot2(pr, ones, lt[kb]);
         }
         pb[2 * kb + g] = v;
       }
@@ -295,7 +327,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
   LBM_WAIT_VMCNT_LDS0(0);
   barrier();
   f32x16 s_a[2], s_b[2];
-  bf16x8 kf[8];  // K operands of the next tile position's K Q^T
+  h8 kf[8];  // K operands of the next tile position's K Q^T
   k_reads(lds_k[0], kf);
   qk(kf, s_a, neg_m);
   k_reads(lds_k[1], kf);
@@ -311,7 +343,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
   // never underflows.
   // s_nxt (nullable): the next tile's scores, already issued relative to the
   // old max, are moved to the new one.
-  auto refresh_max = [&](const f32x16* s_cur, f32x16* s_nxt, bf16x8* pb, float& lt, bool first)
+  auto refresh_max = [&](const f32x16* s_cur, f32x16* s_nxt, h8* pb, float& lt, bool first)
                          __attribute__((always_inline)) {
     if (__ballot(!(lt <= 256.f)) || first) {
       float mx = s_cur[0][0];
@@ -340,12 +372,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
     }
   };
   // O^T[d][row] += V^T[d][keys] P^T[keys][row]
-  auto pv = [&](const bf16x8* vf, const bf16x8* pb) __attribute__((always_inline)) {
+  auto pv = [&](const h8* vf, const h8* pb) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int G = 0; G < 4; ++G)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db * 4 + G], pb[G], o[db], 0, 0, 0);
+        o[db] = Elt<T>::mfma(vf[db * 4 + G], pb[G], o[db]);
   };
 
   // Steady-state step for tile position i (not the split's last): s_cur
@@ -361,7 +393,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
   auto step = [&](int32_t i, f32x16* s_cur, f32x16* s_nxt) __attribute__((always_inline)) {
     const uint2 code_k = codes_of(i + NST);
     load_codes(i + 2 * NST);
-    bf16x8 vf[8], pb[4];
+    h8 vf[8], pb[4];
     v_reads(lds_v[i & (NST - 1)], vf);
     load_k(i & (NST - 1), code_k);
     load_v((i + NST - 1) & (NST - 1), code_v);
@@ -400,7 +432,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
         for (int e = 0; e < 16; ++e)
           s_cur[kb][e] = kb * 32 + 8 * (e >> 2) + (e & 3) >= lim ? -INFINITY : s_cur[kb][e];
     }
-    bf16x8 vf[8], pb[4];
+    h8 vf[8], pb[4];
     v_reads(lds_v[i & (NST - 1)], vf);
     float lt = exponentiate(s_cur, 0.f, pb);
     refresh_max(s_cur, nullptr, pb, lt, i == 0);
@@ -429,16 +461,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
   if (a.num_splits == 1) {
     if (qrow < a.Tq) {
       const float inv = 1.f / l_tot;
-      __bf16* op = reinterpret_cast<__bf16*>(a.out) + size_t(qrow) * HD + head * D;
+      T* op = reinterpret_cast<T*>(a.out) + size_t(qrow) * HD + head * D;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-          bf16x4 w;
+          typedef T h4 __attribute__((ext_vector_type(4)));
+          h4 w;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) w[j] = static_cast<__bf16>(o[db][4 * i + j] * inv);
-          *reinterpret_cast<bf16x4*>(op + db * 32 + 8 * i + 4 * hh) = w;
+          for (int j = 0; j < 4; ++j) w[j] = static_cast<T>(o[db][4 * i + j] * inv);
+          *reinterpret_cast<h4*>(op + db * 32 + 8 * i + 4 * hh) = w;
         }
     }
     return;
@@ -459,15 +491,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_d64_kernel(const AttnAr
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream) {
+hipError_t launch_attn16(const AttnArgs& a, int32_t head_dim, bool fp16, hipStream_t stream) {
   if (head_dim != 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_bf16_d64_kernel, dim3(8 * a.items_per_xcd), dim3(kThreads), 0, stream, a);
+  if (fp16)
+    hipLaunchKernelGGL(attn_d64_kernel<_Float16>, dim3(8 * a.items_per_xcd), dim3(kThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL(attn_d64_kernel<__bf16>, dim3(8 * a.items_per_xcd), dim3(kThreads), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
-int32_t attn_occupancy_bf16() {
+int32_t attn_occupancy16() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_d64_kernel, kThreads, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_d64_kernel<__bf16>, kThreads, 0) !=
           hipSuccess ||
       n < 1)
     return 1;

@@ -69,7 +69,8 @@ struct AttnArgs {
 // Fill the split/grid fields of `a` for a launch (Tq, kv_len, splits known).
 void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits);
 
-hipError_t launch_attn_bf16(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
+// 16-bit inputs: bf16, or fp16 when `fp16`
+hipError_t launch_attn16(const AttnArgs& a, int32_t head_dim, bool fp16, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
 
 // Combine the key-range splits' partials into the output (after an attention

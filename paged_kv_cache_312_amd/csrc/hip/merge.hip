@@ -51,6 +51,8 @@ hipError_t launch_merge(const AttnArgs& a, int32_t head_dim, int32_t dtype, hipS
   const dim3 grid(uint32_t((total + 255) / 256)), block(256);
   if (dtype == LBM_BF16 && head_dim == 64)
     hipLaunchKernelGGL((merge_kernel<__bf16, 64>), grid, block, 0, stream, a);
+  else if (dtype == LBM_F16 && head_dim == 64)
+    hipLaunchKernelGGL((merge_kernel<_Float16, 64>), grid, block, 0, stream, a);
   else if (dtype == LBM_F32 && head_dim == 64)
     hipLaunchKernelGGL((merge_kernel<float, 64>), grid, block, 0, stream, a);
   else if (dtype == LBM_F32 && head_dim == 32)

@@ -24,6 +24,12 @@ BF16_MAX_ABS = 2e-2      # stated tolerance for bf16
 BF16_REL_L2 = 1e-2       # self-gate (catches a dropped page the max-abs bound misses)
 F32_MAX_ABS = 1e-5       # stated tolerance for fp32
 F32_REL_L2 = 1e-5
+# fp16: the bf16 bounds scaled by the ratio of unit roundoffs, 2^-12 / 2^-9
+# (P, q*log2(e)/sqrt(D) and the output are rounded to fp16 instead of bf16)
+F16_MAX_ABS = BF16_MAX_ABS / 8
+F16_REL_L2 = BF16_REL_L2 / 8
+TOLERANCES = {"bf16": (BF16_MAX_ABS, BF16_REL_L2), "f16": (F16_MAX_ABS, F16_REL_L2),
+              "f32": (F32_MAX_ABS, F32_REL_L2)}
 
 
 def say(*a):
@@ -84,7 +90,7 @@ def compare(out_gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str) -> dict
     err = np.abs(out_gpu - ref)
     max_abs = float(err.max())
     rel = float(np.linalg.norm(out_gpu - ref) / max(np.linalg.norm(ref), 1e-300))
-    lim_abs, lim_rel = (BF16_MAX_ABS, BF16_REL_L2) if dtype == "bf16" else (F32_MAX_ABS, F32_REL_L2)
+    lim_abs, lim_rel = TOLERANCES[dtype]
     assert np.isfinite(out_gpu).all(), f"{what}: non-finite output"
     assert max_abs <= lim_abs, f"{what}: max-abs {max_abs:.3e} > {lim_abs}"
     assert rel <= lim_rel, f"{what}: rel-L2 {rel:.3e} > {lim_rel}"

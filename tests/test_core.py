@@ -60,6 +60,14 @@ def test_core_matches_reference_allocator(cid):
     _lockstep(workloads.get_config(cid))
 
 
+def test_core_matches_reference_no_scale_frames():
+    """include_scale_frames=False of the pages' eviction call (scale_frames = 0):
+    every frame ages out of the window."""
+    core, ref = _lockstep(workloads.get_config(1).replace(scale_frames=0, total_frames=150))
+    st = core.stats()
+    assert st["scale_pages"] == 0 and st["live_pages"] == 64
+
+
 def test_core_matches_reference_long_stream():
     """10,000 frames: ~9,900 evictions and 3,750 special pages."""
     core, ref = _lockstep(workloads.get_config(3), check_every=61)

@@ -4,7 +4,8 @@ Small streams are checked on every step and every output; the ViT-L-shaped
 workloads run their whole schedules (bookkeeping checked bit-exact) and are
 checked on sampled steps, blocks and query rows -- the rows always include the
 first and the last (ragged tail) one.  Tolerances: bf16 max-abs 2e-2 and
-rel-L2 1e-2; fp32 max-abs 1e-5 and rel-L2 1e-5.
+rel-L2 1e-2; fp16 max-abs 2.5e-3 and rel-L2 1.25e-3; fp32 max-abs 1e-5 and
+rel-L2 1e-5.
 """
 import pytest
 
@@ -20,6 +21,10 @@ ODD_BF16 = workloads.StreamConfig(
 ODD_F32 = ODD_BF16.replace(name="odd_f32", cid=13, dtype="f32")
 ODD_F32_D32 = ODD_BF16.replace(name="odd_f32_d32", cid=14, dtype="f32", head_dim=32,
                                patches_per_frame=37, special_per_frame=3, special_page_size=8)
+ODD_F16 = ODD_BF16.replace(name="odd_f16", cid=15, dtype="f16")
+# include_scale_frames=False of the pages' eviction call: no frame is kept
+# beyond the window (scale_frames = 0)
+ODD_NO_SCALE = ODD_BF16.replace(name="odd_no_scale", cid=16, scale_frames=0)
 
 
 def test_tiny_config_every_output():
@@ -28,7 +33,8 @@ def test_tiny_config_every_output():
 
 
 @pytest.mark.parametrize("splits", [0, 1, 3])
-@pytest.mark.parametrize("cfg", [ODD_BF16, ODD_F32, ODD_F32_D32], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [ODD_BF16, ODD_F16, ODD_F32, ODD_F32_D32, ODD_NO_SCALE],
+                         ids=lambda c: c.name)
 def test_small_streams_every_output(cfg, splits):
     w = run_stream(cfg, num_splits=splits, label=f"{cfg.name}/splits={splits}")
     say(cfg.name, splits, w)
@@ -48,6 +54,20 @@ def test_vitl_single_block_stream():
     checks = {0, 1, 63, 64, 65, 120, 200}          # F = 8, 9, 71, 72, 73, 128, 208
     w = run_stream(cfg, check_steps=checks, rows_per_check=96, label="vitl_single_block")
     say("C1", w)
+
+
+def test_vitl_single_block_f16_stream():
+    """The fp16 kernel on the ViT-L shape: window filling and full."""
+    cfg = workloads.get_config(1).replace(dtype="f16", total_frames=90)
+    w = run_stream(cfg, check_steps={0, 63, 64, 81}, rows_per_check=96, label="vitl_f16")
+    say("C1 f16", w)
+
+
+def test_vitl_single_block_no_scale_frames():
+    """include_scale_frames=False (scale_frames = 0) at the ViT-L shape."""
+    cfg = workloads.get_config(1).replace(scale_frames=0, total_frames=80)
+    w = run_stream(cfg, check_steps={0, 56, 71}, rows_per_check=64, label="vitl_no_scale")
+    say("C1 no scale", w)
 
 
 def test_vitl_single_block_peaky_queries():
