@@ -144,7 +144,8 @@ def pmc_summary(fetch_dir, write_dir):
     with open(TRAFFIC_RECORD, "w") as fh:
         fh.write("HBM traffic of one lbm_run (attention + merge), 24-block ViT-L step; written by "
                  "'bench.py --pmc-summary' from two rocprofv3 --pmc runs of 'bench.py --steps 2 "
-                 "--warmup 0 --no-cpu-baseline --calibrate-copy' (FETCH_SIZE, then WRITE_SIZE)\n")
+                 "--warmup 0 --no-cpu-baseline --no-variants --calibrate-copy' (FETCH_SIZE, "
+                 "then WRITE_SIZE)\n")
         fh.write(json.dumps(rec, indent=1) + "\n")
     print(json.dumps(rec))
 
