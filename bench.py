@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--variant-steps", type=int, default=100,
                     help="timed steps of the same workload in fp16 (reported under 'variants')")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--skip-steps", type=int, default=50,
+                    help="skip-append frames timed after the run (reported under 'variants')")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the run, stream a 1 GiB buffer through a plain elementwise copy "
                          "three times (reference for the HBM byte counters)")
@@ -151,12 +153,14 @@ def pmc_summary(fetch_dir, write_dir):
 
 
 
-def measure_stream(cfg, dev, steps, warmup, splits_req=0, keep=False):
+def measure_stream(cfg, dev, steps, warmup, splits_req=0, keep=False, skip_steps=0):
     """Stream ``cfg`` through its first step and the window fill, ``warmup``
     more steps, then time ``steps`` frame steps (all blocks: append, evict and
     plan once, attention), with HIP events around every lbm_run and every
-    append of one further step.  Returns the figures (and, with ``keep``, the
-    live cache and inputs for the CPU baseline)."""
+    append of one further step; then ``skip_steps`` skip-append frames (each
+    frame's queries over the visible set and its own rows, nothing stored).
+    Returns the figures (and, with ``keep``, the live cache and inputs for the
+    CPU baseline)."""
     import torch
 
     import paged_kv_cache_312_amd as lbm
@@ -251,10 +255,33 @@ def measure_stream(cfg, dev, steps, warmup, splits_req=0, keep=False):
     app_bytes = 2 * 2 * T * H * D * cache.dtype.itemsize  # K and V rows, read + write
     append_gbps = app_bytes / (app_ms * 1e-3) / 1e9
 
+    skip = None
+    if skip_steps > 0:
+        kv_cache = cache.get_plan()[0]
+        ev_s = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+                 for _ in range(B)] for _ in range(skip_steps)]
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(skip_steps):
+            inputs = sets[(step_idx + 1 + i) % N_INPUT_SETS]
+            cache.plan_transient(T, T)
+            for b in range(B):
+                q, k, v = inputs[b]
+                ev_s[i][b][0].record(stream)
+                cache.run_transient(b, q, k, v, outs[b])
+                ev_s[i][b][1].record(stream)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t1
+        s_ms = sum(e0.elapsed_time(e1) for row in ev_s for e0, e1 in row)
+        s_flops = skip_steps * B * 4.0 * T * (kv_cache + T) * H * D
+        skip = {"fps": skip_steps / el, "tflops": s_flops / (s_ms * 1e-3) / 1e12,
+                "avg_launch_ms": s_ms / (skip_steps * B), "kv_len": kv_cache + T}
+        assert cache.stats()["frame_count"] == F + 1   # nothing appended by the skip frames
+
     res = {"fps": fps, "ms_per_step": ms_per_step, "tflops": achieved_tflops,
            "avg_launch_ms": avg_launch_ms, "flops": flops, "n_launch": n_launch,
            "kv_lens": kv_lens, "splits": splits, "F_first": F_first, "F_last": F,
-           "app_ms": app_ms, "app_bytes": app_bytes, "append_gbps": append_gbps}
+           "app_ms": app_ms, "app_bytes": app_bytes, "append_gbps": append_gbps, "skip": skip}
     if keep:
         res.update(_cache=cache, _init=init, _sets=sets, _F=F)
     else:
@@ -279,7 +306,8 @@ def main():
     cfg = workloads.get_config("vitl_24_block_frame_step")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    m = measure_stream(cfg, dev, args.steps, args.warmup, args.splits, keep=True)
+    m = measure_stream(cfg, dev, args.steps, args.warmup, args.splits, keep=True,
+                       skip_steps=0 if args.no_variants else args.skip_steps)
     B, H, D, T = cfg.num_blocks, cfg.num_heads, cfg.head_dim, cfg.tokens_per_frame
     cache, init, sets, F = m.pop("_cache"), m.pop("_init"), m.pop("_sets"), m.pop("_F")
     kv_lens, splits = m["kv_lens"], m["splits"]
@@ -320,17 +348,24 @@ def main():
     }
 
     cache.close()
+    if m["skip"] is not None:
+        sk = m["skip"]
+        result["variants"] = {"skip_append_bf16": {
+            "value": round(sk["fps"], 3), "unit": "frames/s", "steps": args.skip_steps,
+            "kv_len": sk["kv_len"], "attention_tflops": round(sk["tflops"], 2),
+            "frac": round(sk["tflops"] / PEAK_BF16_TFLOPS, 4), "peak": PEAK_BF16_TFLOPS,
+            "avg_launch_ms": round(sk["avg_launch_ms"], 4)}}
     if not args.no_variants:
         # the same 24-block stream with fp16 storage and MFMA (the pages' other
         # 16-bit type); a shorter timed run after the same fill
         v = measure_stream(cfg.replace(dtype="f16"), dev, args.variant_steps, args.warmup,
                            args.splits)
-        result["variants"] = {"fp16": {
+        result.setdefault("variants", {})["fp16"] = {
             "value": round(v["fps"], 3), "unit": "frames/s", "steps": args.variant_steps,
             "timed_frames": [v["F_first"], v["F_last"]],
             "attention_tflops": round(v["tflops"], 2),
             "frac": round(v["tflops"] / PEAK_FP16_TFLOPS, 4), "peak": PEAK_FP16_TFLOPS,
-            "avg_launch_ms": round(v["avg_launch_ms"], 4), "key_splits": v["splits"]}}
+            "avg_launch_ms": round(v["avg_launch_ms"], 4), "key_splits": v["splits"]}
 
     if args.calibrate_copy:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)

@@ -180,6 +180,30 @@ lbm_status lbm_plan(lbm_cache* cache, int32_t num_q_tokens, void* hip_stream);
 lbm_status lbm_run(lbm_cache* cache, int32_t block_idx, const void* q, void* out,
                    int32_t num_q_tokens, void* hip_stream);
 
+/* Skip-append step: a frame processed without storing its K/V ([P1]
+ * "Implementation Examples": non-key frames skip the append; [P3] "Manual
+ * Cache Control for Advanced Use Cases": a frame processed without storing
+ * its KV).  Plans the visible set of the cache as it stands followed by
+ * num_own_tokens rows of the frame itself (1..max_q_tokens), which
+ * lbm_run_transient reads from the caller's k/v instead of the pools.  The
+ * bookkeeping is unchanged: no page is reserved, nothing is written, the stats
+ * and the next frame's visible set are as if the frame never came.  That the
+ * frame attends to its own tokens is the plain reading of a block computing
+ * attention over the cache and the current tokens (the pages do not say).
+ * Same preconditions as lbm_plan; with a step open, every block must have
+ * appended it.  Errors: INVALID_ARG, BAD_STATE. */
+lbm_status lbm_plan_transient(lbm_cache* cache, int32_t num_q_tokens, int32_t num_own_tokens,
+                              void* hip_stream);
+
+/* Attention of one block for a skip-append plan: out = softmax(q K^T/sqrt(D)) V
+ * over the visible tokens then the frame's own rows k, v (device
+ * [num_own_tokens, H, D] in the config dtype, 16-byte aligned; read only, never
+ * stored).  q, out as for lbm_run.  Errors: INVALID_ARG, BAD_STATE (no plan, a
+ * stale plan, a normal plan, a different num_q_tokens).  lbm_run refuses a
+ * skip-append plan. */
+lbm_status lbm_run_transient(lbm_cache* cache, int32_t block_idx, const void* q, const void* k,
+                             const void* v, void* out, int32_t num_q_tokens, void* hip_stream);
+
 /* Stateless paged attention over caller-given tables (device int32 arrays):
  * the visible keys are the n_patch_pages patch pages listed in patch_ids
  * (each P tokens) followed by the first n_special_tokens tokens of the

@@ -111,6 +111,26 @@ class StreamOracle:
             qq = qq[np.asarray(rows)]
         return dense_attention(qq, K, V)
 
+    def skip_append_outputs(self, block: int, q: np.ndarray, k_own: np.ndarray,
+                            v_own: np.ndarray, rows: Optional[np.ndarray] = None,
+                            heads: Optional[List[int]] = None):
+        """Outputs of a frame processed without storing its K/V (skip-append,
+        [P1] "Implementation Examples"; [P3] "Manual Cache Control for Advanced
+        Use Cases"): q, k_own, v_own are the frame's [T', H, D] rows.  Its
+        queries attend over the visible set of the F accepted frames followed
+        by its own rows; the history and F are unchanged.  The pages say only
+        that such a frame's K/V is not written to the cache; that it still
+        attends to its own tokens is the plain reading of a block that
+        computes attention over the cache and the current tokens."""
+        hs = list(range(q.shape[1])) if heads is None else list(heads)
+        K, V = self.visible_kv(block, self.F, None if heads is None else hs)
+        K = np.concatenate([K, np.asarray(k_own, np.float64)[:, hs, :]], axis=0)
+        V = np.concatenate([V, np.asarray(v_own, np.float64)[:, hs, :]], axis=0)
+        qq = np.asarray(q, np.float64)[:, hs, :]
+        if rows is not None:
+            qq = qq[np.asarray(rows)]
+        return dense_attention(qq, K, V)
+
     def commit(self, block_kv: Dict[int, Tuple[np.ndarray, np.ndarray]], nf: int) -> None:
         """Accept the step: store each block's new frames in the history."""
         for b, (k_new, v_new) in block_kv.items():

@@ -18,7 +18,8 @@ __all__ = [
     "LBM_BF16", "LBM_F16", "LBM_F32", "LbmConfig", "LbmError", "LbmStats", "make_config",
     "lbm_query_sizes", "lbm_cache_create", "lbm_cache_destroy", "lbm_cache_reset",
     "lbm_cache_seed_free_lists", "lbm_append_frame", "lbm_evict_frames",
-    "lbm_rollback_last_frame", "lbm_plan", "lbm_run", "lbm_paged_attention", "lbm_get_stats",
+    "lbm_rollback_last_frame", "lbm_plan", "lbm_run", "lbm_plan_transient", "lbm_run_transient",
+    "lbm_paged_attention", "lbm_get_stats",
     "lbm_dump_state", "lbm_get_plan", "lbm_plan_num_splits", "lbm_last_error",
     "PagedKVCache", "CoreBookkeeping",
 ]
@@ -117,6 +118,18 @@ def lbm_run(handle: int, block_idx: int, q: int, out: int, num_q_tokens: int,
             stream: int) -> None:
     _ck(lib().lbm_run(c_void_p(handle), block_idx, c_void_p(q), c_void_p(out), num_q_tokens,
                       c_void_p(stream)), "lbm_run")
+
+
+def lbm_plan_transient(handle: int, num_q_tokens: int, num_own_tokens: int, stream: int) -> None:
+    _ck(lib().lbm_plan_transient(c_void_p(handle), num_q_tokens, num_own_tokens,
+                                 c_void_p(stream)), "lbm_plan_transient")
+
+
+def lbm_run_transient(handle: int, block_idx: int, q: int, k: int, v: int, out: int,
+                      num_q_tokens: int, stream: int) -> None:
+    _ck(lib().lbm_run_transient(c_void_p(handle), block_idx, c_void_p(q), c_void_p(k),
+                                c_void_p(v), c_void_p(out), num_q_tokens, c_void_p(stream)),
+        "lbm_run_transient")
 
 
 def lbm_paged_attention(cfg: LbmConfig, q: int, out: int, num_q_tokens: int, patch_pool: int,
@@ -227,6 +240,7 @@ class PagedKVCache:
         lbm_rollback_last_frame(self.handle)
 
     def plan(self, num_q_tokens: int, stream=None) -> None:
+        self._own_rows = None
         lbm_plan(self.handle, num_q_tokens, self._stream(stream))
 
     def run(self, block_idx: int, q, out=None, stream=None):
@@ -237,6 +251,28 @@ class PagedKVCache:
             self._check_tensor(out, q.shape[0])
         lbm_run(self.handle, block_idx, q.data_ptr(), out.data_ptr(), q.shape[0],
                 self._stream(stream))
+        return out
+
+    def plan_transient(self, num_q_tokens: int, num_own_tokens: int, stream=None) -> None:
+        """Plan a skip-append step (the frame's own rows follow the visible set)."""
+        self._own_rows = None
+        lbm_plan_transient(self.handle, num_q_tokens, num_own_tokens, self._stream(stream))
+        self._own_rows = num_own_tokens
+
+    def run_transient(self, block_idx: int, q, k, v, out=None, stream=None):
+        """Attention of a skip-append step: q over the visible set and the
+        frame's own k, v rows, which are never stored."""
+        self._check_tensor(q)
+        # the library reads exactly the planned number of own rows from k and v
+        # (without a skip-append plan it refuses the call before any launch)
+        self._check_tensor(k, getattr(self, "_own_rows", None))
+        self._check_tensor(v, k.shape[0])
+        if out is None:
+            out = self.torch.empty_like(q)
+        else:
+            self._check_tensor(out, q.shape[0])
+        lbm_run_transient(self.handle, block_idx, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                          out.data_ptr(), q.shape[0], self._stream(stream))
         return out
 
     def reset(self) -> None:

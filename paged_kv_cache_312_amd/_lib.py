@@ -58,6 +58,9 @@ LBM_FUNCS = {
     "lbm_rollback_last_frame": (c_int32, [c_void_p]),
     "lbm_plan": (c_int32, [c_void_p, c_int32, c_void_p]),
     "lbm_run": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p]),
+    "lbm_plan_transient": (c_int32, [c_void_p, c_int32, c_int32, c_void_p]),
+    "lbm_run_transient": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                    c_int32, c_void_p]),
     "lbm_paged_attention": (c_int32, [POINTER(LbmConfig), c_void_p, c_void_p, c_int32, c_void_p,
                                       c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p,
                                       c_void_p]),

@@ -70,8 +70,9 @@ lbm_status validate_config(const lbm_config& c) {
     return fail(LBM_ERR_UNSUPPORTED, "one append may touch %lld special pages (> %d)",
                 (long long)sp_touch, kMaxStepSpecialPages);
   // every visible key position must stay below 2^24
+  // visible keys at most, plus the own rows of a skip-append step
   const int64_t max_kv = int64_t(c.scale_frames + c.sliding_window) * c.patches_per_frame +
-                         int64_t(c.max_special_pages) * c.special_page_size;
+                         int64_t(c.max_special_pages) * c.special_page_size + c.max_q_tokens;
   if (max_kv >= kMaxKvLen)
     return fail(LBM_ERR_UNSUPPORTED, "visible key range %lld exceeds %d", (long long)max_kv,
                 kMaxKvLen);
@@ -339,8 +340,9 @@ WorkspaceLayout workspace_layout(const lbm_config& c) {
   off = align_up(off + sizeof(int32_t) * size_t(std::max(1, c.scale_frames + c.sliding_window)), 256);
   w.special_ids_off = off;
   off = align_up(off + sizeof(int32_t) * size_t(std::max(1, c.max_special_pages)), 256);
+  // visible keys at most, plus the own rows of a skip-append step
   const int64_t max_kv = int64_t(c.scale_frames + c.sliding_window) * c.patches_per_frame +
-                        int64_t(c.max_special_pages) * c.special_page_size;
+                         int64_t(c.max_special_pages) * c.special_page_size + c.max_q_tokens;
   w.rowtab_len = int32_t((max_kv + kKeysPerTile - 1) / kKeysPerTile * kKeysPerTile);
   if (w.rowtab_len < kKeysPerTile) w.rowtab_len = kKeysPerTile;
   w.rowtab_off = off;

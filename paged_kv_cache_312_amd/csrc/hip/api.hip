@@ -77,6 +77,7 @@ struct lbm_cache {
   uint64_t plan_epoch = 0;
   int32_t plan_q = 0;
   int32_t plan_splits = 0;
+  int32_t plan_own = 0;       // own rows of a skip-append step planned (0: a normal plan)
   PlanInfo plan;
 
   // pinned staging of the table, double-buffered and guarded by events
@@ -104,9 +105,11 @@ lbm_status copy_record(const std::vector<int32_t>& v, int32_t* buf, int64_t cap,
 
 // Row table of the visible set described by (patch ids, special ids) into
 // `rowtab`, then the attention launch; both on stream `st`.
+// Positions past kv_len (up to the tile boundary of kv_len + own, the own
+// rows of a skip-append step included) get position 0's code.
 lbm_status launch_rowtab_for(const lbm_config& c, const int32_t* pids, const int32_t* sids,
-                             int32_t patch_tokens, int32_t kv_len, uint32_t* rowtab,
-                             hipStream_t st) {
+                             int32_t patch_tokens, int32_t kv_len, int32_t own,
+                             uint32_t* rowtab, hipStream_t st) {
   RowtabArgs r;
   std::memset(&r, 0, sizeof(r));
   r.patch_ids = pids;
@@ -116,7 +119,7 @@ lbm_status launch_rowtab_for(const lbm_config& c, const int32_t* pids, const int
   r.SPS = c.special_page_size;
   r.patch_tokens = patch_tokens;
   r.kv_len = kv_len;
-  r.n_pos = (kv_len + kKeysPerTile - 1) / kKeysPerTile * kKeysPerTile;
+  r.n_pos = (kv_len + own + kKeysPerTile - 1) / kKeysPerTile * kKeysPerTile;
   r.row_bytes = int32_t(size_t(c.num_heads) * c.head_dim * dtype_size(c.dtype));
   r.inv_P = 1.0f / float(r.P);
   r.inv_SPS = 1.0f / float(r.SPS);
@@ -142,13 +145,15 @@ AttnArgs base_args(const lbm_config& c, const void* q, void* out, int32_t nq, co
   const int64_t row_bytes = int64_t(c.num_heads) * c.head_dim * int64_t(dtype_size(c.dtype));
   a.vstride_patch = int32_t(c.patches_per_frame * row_bytes);
   a.vstride_special = int32_t(c.special_page_size * row_bytes);
+  a.row_bytes = int32_t(row_bytes);
   return a;
 }
 
 lbm_status launch_attention(const lbm_config& c, AttnArgs* a, int32_t splits, hipStream_t st) {
   finish_attn_args(a, c.head_dim, splits);
-  hipError_t e = c.dtype == LBM_F32 ? launch_attn_f32(*a, c.head_dim, st)
-                                    : launch_attn16(*a, c.head_dim, c.dtype == LBM_F16, st);
+  const bool own = a->tr_start < a->kv_len;
+  hipError_t e = c.dtype == LBM_F32 ? launch_attn_f32(*a, c.head_dim, own, st)
+                                    : launch_attn16(*a, c.head_dim, c.dtype == LBM_F16, own, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   if (a->num_splits > 1) {
     e = launch_merge(*a, c.head_dim, c.dtype, st);
@@ -340,10 +345,12 @@ lbm_status lbm_rollback_last_frame(lbm_cache* c) {
   return LBM_OK;
 }
 
-lbm_status lbm_plan(lbm_cache* c, int32_t num_q_tokens, void* hip_stream) {
-  clear_error();
-  lbm_status st = check_cache(c);
-  if (st != LBM_OK) return st;
+namespace {
+
+// The plan of a frame step: the visible set of the cache as it stands, plus
+// `own` rows of the frame itself on a skip-append step (they follow the
+// special stream).
+lbm_status plan_impl(lbm_cache* c, int32_t num_q_tokens, int32_t own, void* hip_stream) {
   if (num_q_tokens < 1 || num_q_tokens > c->cfg.max_q_tokens)
     return fail(LBM_ERR_INVALID_ARG, "num_q_tokens %d outside 1..%d", num_q_tokens,
                 c->cfg.max_q_tokens);
@@ -376,19 +383,45 @@ lbm_status lbm_plan(lbm_cache* c, int32_t num_q_tokens, void* hip_stream) {
   lbm_status rs = launch_rowtab_for(
       c->cfg, reinterpret_cast<const int32_t*>(c->workspace + c->ws.patch_ids_off),
       reinterpret_cast<const int32_t*>(c->workspace + c->ws.special_ids_off), p.patch_tokens,
-      p.kv_len, reinterpret_cast<uint32_t*>(c->workspace + c->ws.rowtab_off), s);
+      p.kv_len, own, reinterpret_cast<uint32_t*>(c->workspace + c->ws.rowtab_off), s);
   if (rs != LBM_OK) return rs;
 
   const int32_t cap = split_capacity(c->ws, num_q_tokens);
-  int32_t ns = choose_splits(num_q_tokens, p.kv_len, c->cfg.num_heads, c->num_cu, c->wg_per_cu,
-                             cap, c->cfg.num_splits);
+  int32_t ns = choose_splits(num_q_tokens, p.kv_len + own, c->cfg.num_heads, c->num_cu,
+                             c->wg_per_cu, cap, c->cfg.num_splits);
   if (ns < 1) ns = 1;
   c->plan = p;
   c->plan_q = num_q_tokens;
   c->plan_splits = ns;
+  c->plan_own = own;
   c->plan_epoch = c->bk.epoch();
   c->plan_valid = true;
   return LBM_OK;
+}
+
+}  // namespace
+
+lbm_status lbm_plan(lbm_cache* c, int32_t num_q_tokens, void* hip_stream) {
+  clear_error();
+  lbm_status st = check_cache(c);
+  if (st != LBM_OK) return st;
+  return plan_impl(c, num_q_tokens, 0, hip_stream);
+}
+
+lbm_status lbm_plan_transient(lbm_cache* c, int32_t num_q_tokens, int32_t num_own_tokens,
+                              void* hip_stream) {
+  clear_error();
+  lbm_status st = check_cache(c);
+  if (st != LBM_OK) return st;
+  if (num_own_tokens < 1 || num_own_tokens > c->cfg.max_q_tokens)
+    return fail(LBM_ERR_INVALID_ARG, "num_own_tokens %d outside 1..%d", num_own_tokens,
+                c->cfg.max_q_tokens);
+  if (c->step_open) {
+    for (int32_t b = 0; b < c->cfg.num_blocks; ++b)
+      if (!c->appended[size_t(b)])
+        return fail(LBM_ERR_BAD_STATE, "block %d has not appended the open step", b);
+  }
+  return plan_impl(c, num_q_tokens, num_own_tokens, hip_stream);
 }
 
 int32_t lbm_plan_num_splits(const lbm_cache* c) {
@@ -411,11 +444,39 @@ lbm_status lbm_run(lbm_cache* c, int32_t block_idx, const void* q, void* out,
     return fail(LBM_ERR_BAD_STATE, "run with %d queries, plan made for %d", num_q_tokens, c->plan_q);
   if (c->step_open && !c->appended[size_t(block_idx)])
     return fail(LBM_ERR_BAD_STATE, "block %d has not appended the open step", block_idx);
+  if (c->plan_own > 0) return fail(LBM_ERR_BAD_STATE, "the plan is a skip-append plan");
   AttnArgs a = base_args(c->cfg, q, out, num_q_tokens, c->patch_pools[size_t(block_idx)],
                          c->special_pools[size_t(block_idx)],
                          reinterpret_cast<const uint32_t*>(c->workspace + c->ws.rowtab_off),
                          c->workspace, c->ws);
   a.kv_len = c->plan.kv_len;
+  a.tr_start = a.kv_len;
+  return launch_attention(c->cfg, &a, c->plan_splits, static_cast<hipStream_t>(hip_stream));
+}
+
+lbm_status lbm_run_transient(lbm_cache* c, int32_t block_idx, const void* q, const void* k,
+                             const void* v, void* out, int32_t num_q_tokens, void* hip_stream) {
+  clear_error();
+  lbm_status st = check_cache(c);
+  if (st != LBM_OK) return st;
+  if (block_idx < 0 || block_idx >= c->cfg.num_blocks)
+    return fail(LBM_ERR_INVALID_ARG, "block_idx %d outside 0..%d", block_idx, c->cfg.num_blocks - 1);
+  if (!q || !out || !k || !v || !aligned16(q) || !aligned16(out) || !aligned16(k) || !aligned16(v))
+    return fail(LBM_ERR_INVALID_ARG, "q/k/v/out null or not 16-byte aligned");
+  if (!c->plan_valid) return fail(LBM_ERR_BAD_STATE, "run without a plan");
+  if (c->plan_epoch != c->bk.epoch())
+    return fail(LBM_ERR_BAD_STATE, "plan is stale (append, evict or rollback since)");
+  if (c->plan_own < 1) return fail(LBM_ERR_BAD_STATE, "the plan is not a skip-append plan");
+  if (num_q_tokens != c->plan_q)
+    return fail(LBM_ERR_BAD_STATE, "run with %d queries, plan made for %d", num_q_tokens, c->plan_q);
+  AttnArgs a = base_args(c->cfg, q, out, num_q_tokens, c->patch_pools[size_t(block_idx)],
+                         c->special_pools[size_t(block_idx)],
+                         reinterpret_cast<const uint32_t*>(c->workspace + c->ws.rowtab_off),
+                         c->workspace, c->ws);
+  a.tr_start = c->plan.kv_len;
+  a.kv_len = c->plan.kv_len + c->plan_own;
+  a.tk = k;
+  a.tv = v;
   return launch_attention(c->cfg, &a, c->plan_splits, static_cast<hipStream_t>(hip_stream));
 }
 
@@ -450,10 +511,11 @@ lbm_status lbm_paged_attention(const lbm_config* cfg, const void* q, void* out,
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   uint32_t* rowtab = reinterpret_cast<uint32_t*>(wb + ws.rowtab_off);
   st = launch_rowtab_for(*cfg, patch_ids, special_ids, n_patch_pages * cfg->patches_per_frame,
-                         int32_t(kv), rowtab, stream);
+                         int32_t(kv), 0, rowtab, stream);
   if (st != LBM_OK) return st;
   AttnArgs a = base_args(*cfg, q, out, num_q_tokens, patch_pool, special_pool, rowtab, wb, ws);
   a.kv_len = int32_t(kv);
+  a.tr_start = a.kv_len;
   int dev = 0, ncu = 256;
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);

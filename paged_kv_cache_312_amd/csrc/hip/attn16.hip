@@ -133,8 +133,9 @@ __device__ __forceinline__ V8 v_operand(const uint16_t* p0, const uint16_t* p1) 
   return __builtin_bit_cast(V8, both);
 }
 
-// one kernel per element type: attn_d64_kernel<__bf16> and attn_d64_kernel<_Float16>
-template <typename T>
+// one kernel per element type: attn_d64_kernel<__bf16> and attn_d64_kernel<_Float16>;
+// TR: a skip-append step, whose last keys are the frame's own rows
+template <typename T, bool TR>
 __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const AttnArgs a) {
   typedef typename Elt<T>::v8 h8;
   typedef typename Elt<T>::v2 h2;
@@ -200,13 +201,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const AttnArgs a)
     const int32_t off = v ? v_col + (special ? a.vstride_special : a.vstride_patch) : k_col;
     return base + (code & 0x7fffffffu) + off;
   };
-  auto load_k = [&](int32_t stage, uint2 c) __attribute__((always_inline)) {
-    load_to_lds<16>(row_ptr(c.x, false), &lds_k[stage][(8 * wave) * LS]);
-    load_to_lds<16>(row_ptr(c.y, false), &lds_k[stage][(32 + 8 * wave) * LS]);
+  // Skip-append step: keys in [tr_start, kv_len) of tile position x come from
+  // the frame's own rows (the row table holds position 0's code there, like
+  // the padding past kv_len, which keeps its code).  The test is uniform per
+  // tile, so tiles of cached keys take the plain path.
+  auto own_rows = [&](int32_t x, bool v, const char*& p0, const char*& p1)
+                      __attribute__((always_inline)) {
+    const int32_t t0 = tile_at(x) * 64;
+    if (t0 + 64 > a.tr_start) {
+      const char* base = static_cast<const char*>(v ? a.tv : a.tk) + (v ? v_col : k_col);
+      const int32_t k0 = t0 + lp, k1 = t0 + lp + 32;
+      if (k0 >= a.tr_start && k0 < a.kv_len) p0 = base + size_t(k0 - a.tr_start) * a.row_bytes;
+      if (k1 >= a.tr_start && k1 < a.kv_len) p1 = base + size_t(k1 - a.tr_start) * a.row_bytes;
+    }
   };
-  auto load_v = [&](int32_t stage, uint2 c) __attribute__((always_inline)) {
-    load_to_lds<16>(row_ptr(c.x, true), &lds_v[stage][(8 * wave) * LS]);
-    load_to_lds<16>(row_ptr(c.y, true), &lds_v[stage][(32 + 8 * wave) * LS]);
+  auto load_k = [&](int32_t stage, uint2 c, int32_t x) __attribute__((always_inline)) {
+    const char* p0 = row_ptr(c.x, false);
+    const char* p1 = row_ptr(c.y, false);
+    if (TR) own_rows(x, false, p0, p1);
+    load_to_lds<16>(p0, &lds_k[stage][(8 * wave) * LS]);
+    load_to_lds<16>(p1, &lds_k[stage][(32 + 8 * wave) * LS]);
+  };
+  auto load_v = [&](int32_t stage, uint2 c, int32_t x) __attribute__((always_inline)) {
+    const char* p0 = row_ptr(c.x, true);
+    const char* p1 = row_ptr(c.y, true);
+    if (TR) own_rows(x, true, p0, p1);
+    load_to_lds<16>(p0, &lds_v[stage][(8 * wave) * LS]);
+    load_to_lds<16>(p1, &lds_v[stage][(32 + 8 * wave) * LS]);
   };
   // all 64 codes of tile position x into their slot (every wavefront loads
   // the whole slice, so each one waits only for its own loads)
@@ -320,8 +341,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const AttnArgs a)
 #pragma unroll
   for (int x = 0; x < NST; ++x) {
     code_v = codes_of(x);
-    load_k(x, code_v);
-    if (x < NST - 1) load_v(x, code_v);
+    load_k(x, code_v, x);
+    if (x < NST - 1) load_v(x, code_v, x);
   }
   // code_v: position NST-1, for the V load of step 0
   LBM_WAIT_VMCNT_LDS0(0);
@@ -395,8 +416,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const AttnArgs a)
     load_codes(i + 2 * NST);
     h8 vf[8], pb[4];
     v_reads(lds_v[i & (NST - 1)], vf);
-    load_k(i & (NST - 1), code_k);
-    load_v((i + NST - 1) & (NST - 1), code_v);
+    load_k(i & (NST - 1), code_k, i + NST);
+    load_v((i + NST - 1) & (NST - 1), code_v, i + NST - 1);
     qk(kf, s_nxt, neg_m);
     float lt = exponentiate(s_cur, 0.f, pb);
     k_reads(lds_k[(i + 2) & (NST - 1)], kf);
@@ -491,20 +512,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const AttnArgs a)
 
 }  // namespace
 
-hipError_t launch_attn16(const AttnArgs& a, int32_t head_dim, bool fp16, hipStream_t stream) {
+hipError_t launch_attn16(const AttnArgs& a, int32_t head_dim, bool fp16, bool transient,
+                         hipStream_t stream) {
   if (head_dim != 64) return hipErrorInvalidValue;
-  if (fp16)
-    hipLaunchKernelGGL(attn_d64_kernel<_Float16>, dim3(8 * a.items_per_xcd), dim3(kThreads), 0,
-                       stream, a);
+  const dim3 grid(8 * a.items_per_xcd), block(kThreads);
+  if (fp16 && transient)
+    hipLaunchKernelGGL((attn_d64_kernel<_Float16, true>), grid, block, 0, stream, a);
+  else if (fp16)
+    hipLaunchKernelGGL((attn_d64_kernel<_Float16, false>), grid, block, 0, stream, a);
+  else if (transient)
+    hipLaunchKernelGGL((attn_d64_kernel<__bf16, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(attn_d64_kernel<__bf16>, dim3(8 * a.items_per_xcd), dim3(kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((attn_d64_kernel<__bf16, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 int32_t attn_occupancy16() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_d64_kernel<__bf16>, kThreads, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_d64_kernel<__bf16, false>, kThreads, 0) !=
           hipSuccess ||
       n < 1)
     return 1;

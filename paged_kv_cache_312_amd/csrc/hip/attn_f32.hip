@@ -15,7 +15,8 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int D>
+// TR: a skip-append step, whose keys [tr_start, kv_len) are the frame's own rows
+template <int D, bool TR>
 __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnArgs a) {
   constexpr int KS = D + 4;          // LDS row strides (floats)
   constexpr int VS = D + 8;
@@ -65,7 +66,13 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < PASSES; ++r) {
       const char *kp, *vp;
-      kv_rows(a, a.rowtab[t * 64 + r * KPP + lk], col_off, kp, vp);
+      const int32_t key = t * 64 + r * KPP + lk;
+      kv_rows(a, a.rowtab[key], col_off, kp, vp);
+      if (TR && key >= a.tr_start && key < a.kv_len) {
+        const size_t off = size_t(key - a.tr_start) * a.row_bytes + col_off;
+        kp = static_cast<const char*>(a.tk) + off;
+        vp = static_cast<const char*>(a.tv) + off;
+      }
       kreg[r] = *reinterpret_cast<const float4*>(kp);
       vreg[r] = *reinterpret_cast<const float4*>(vp);
     }
@@ -200,12 +207,16 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnArgs a) {
 
 }  // namespace
 
-hipError_t launch_attn_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream) {
+hipError_t launch_attn_f32(const AttnArgs& a, int32_t head_dim, bool transient, hipStream_t stream) {
   const dim3 grid(8 * a.items_per_xcd), block(kThreads);
-  if (head_dim == 64)
-    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, block, 0, stream, a);
+  if (head_dim == 64 && transient)
+    hipLaunchKernelGGL((attn_f32_kernel<64, true>), grid, block, 0, stream, a);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL((attn_f32_kernel<64, false>), grid, block, 0, stream, a);
+  else if (head_dim == 32 && transient)
+    hipLaunchKernelGGL((attn_f32_kernel<32, true>), grid, block, 0, stream, a);
   else if (head_dim == 32)
-    hipLaunchKernelGGL(attn_f32_kernel<32>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_f32_kernel<32, false>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -214,8 +225,10 @@ hipError_t launch_attn_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stre
 int32_t attn_occupancy_f32(int32_t head_dim) {
   int n = 0;
   hipError_t e = head_dim == 32
-                     ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_f32_kernel<32>, kThreads, 0)
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_f32_kernel<64>, kThreads, 0);
+                     ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_f32_kernel<32, false>,
+                                                                   kThreads, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_f32_kernel<64, false>,
+                                                                   kThreads, 0);
   if (e != hipSuccess || n < 1) return 1;
   return n;
 }

@@ -56,7 +56,14 @@ struct AttnArgs {
   int32_t Tq, H;
   int32_t vstride_patch;      // bytes from a K row to its V row: P * H * D * elt
   int32_t vstride_special;    // SPS * H * D * elt
-  int32_t kv_len;             // visible keys
+  int32_t kv_len;             // visible keys (the frame's own rows included on a skip-append step)
+  // Skip-append step: key positions [tr_start, kv_len) are the frame's own
+  // rows, read from tk / tv ([kv_len - tr_start][H][D]) instead of the pools;
+  // tr_start = kv_len otherwise.
+  const void* tk;
+  const void* tv;
+  int32_t tr_start;
+  int32_t row_bytes;          // H * D * element size
   int32_t n_tiles;            // ceil(kv_len / 64)
   int32_t num_splits, tiles_per_split;
   int32_t n_qt;               // ceil(Tq / 128)
@@ -69,9 +76,11 @@ struct AttnArgs {
 // Fill the split/grid fields of `a` for a launch (Tq, kv_len, splits known).
 void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits);
 
-// 16-bit inputs: bf16, or fp16 when `fp16`
-hipError_t launch_attn16(const AttnArgs& a, int32_t head_dim, bool fp16, hipStream_t stream);
-hipError_t launch_attn_f32(const AttnArgs& a, int32_t head_dim, hipStream_t stream);
+// 16-bit inputs: bf16, or fp16 when `fp16`; `transient`: a skip-append step
+// (tr_start < kv_len)
+hipError_t launch_attn16(const AttnArgs& a, int32_t head_dim, bool fp16, bool transient,
+                         hipStream_t stream);
+hipError_t launch_attn_f32(const AttnArgs& a, int32_t head_dim, bool transient, hipStream_t stream);
 
 // Combine the key-range splits' partials into the output (after an attention
 // launch with num_splits > 1, on the same stream).

@@ -113,10 +113,13 @@ def run_stream(cfg: workloads.StreamConfig, check_steps: Optional[Iterable[int]]
                blocks: Optional[Sequence[int]] = None, num_splits: int = 0,
                deferred: bool = False, accept: Optional[List[bool]] = None,
                dump_every: int = 1, q_scale: float = 1.0, run_every_step: bool = False,
-               label: str = "") -> dict:
+               skip_steps: Iterable[int] = (), label: str = "") -> dict:
     """Drive the whole schedule of ``cfg`` through the library; check the
     bookkeeping against the reference allocator and, at the checked steps, the
-    attention outputs against the oracle.  Returns error statistics."""
+    attention outputs against the oracle.  Steps in ``skip_steps`` (single
+    frames) are skip-append frames: planned and run with the frame's own rows,
+    never appended; the bookkeeping must not move.  Returns error statistics."""
+    skip = set(skip_steps)
     sched = workloads.step_schedule(cfg)
     accept = accept or [True] * len(sched)
     check = set(range(len(sched))) if check_steps is None else set(check_steps)
@@ -136,6 +139,36 @@ def run_stream(cfg: workloads.StreamConfig, check_steps: Optional[Iterable[int]]
         for b in range(cfg.num_blocks):
             q, k, v = workloads.gen_step_qkv(cfg, b, s, nf, DEV, q_scale=q_scale)
             step_in[b] = (q, k, v)
+        if s in skip:
+            assert nf == 1 and s > 0
+            before, stats_before = cache.dump_state(), cache.stats()
+            cache.plan_transient(T, T)
+            worst["splits"].add(cache.num_splits())
+            outs = {b: cache.run_transient(b, *step_in[b]) for b in blocks}
+            assert cache.dump_state() == before and cache.stats() == stats_before, \
+                f"{label} step {s}: skip-append moved the bookkeeping"
+            assert ref.dump() == before
+            if do_check:
+                torch.cuda.synchronize()
+                rows = None if rows_per_check is None else sample_rows(T, rows_per_check, s)
+                hs = None if heads is None else list(heads)
+                for b in blocks:
+                    q, k, v = [t.double().cpu().numpy() for t in step_in[b]]
+                    ref_out = orc.skip_append_outputs(b, q, k, v, rows=rows, heads=hs)
+                    g = outs[b].double()
+                    if rows is not None:
+                        g = g[torch.as_tensor(rows, device=g.device)]
+                    if hs is not None:
+                        g = g[:, hs]
+                    st = compare(g.cpu().numpy(), ref_out, cfg.dtype,
+                                 f"{label} skip step {s} block {b}")
+                    worst["max_abs"] = max(worst["max_abs"], st["max_abs"])
+                    worst["rel_l2"] = max(worst["rel_l2"], st["rel_l2"])
+                    worst["checks"] += 1
+                hist.clear_cache()
+                say(f"{label}: skip-append step {s} at F={orc.F} checked, worst so far "
+                    f"max_abs={worst['max_abs']:.3e} rel_l2={worst['rel_l2']:.3e}")
+            continue
         before = ref.dump() if not accept[s] else None
         # protocol: append(0), [evict], plan, run(0), then append(b), run(b)
         outs = {}

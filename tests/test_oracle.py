@@ -389,6 +389,53 @@ def test_stream_oracle_tiny_with_rejects_vs_brute():
     assert worst <= 1e-12
 
 
+def _tiny_oracle_after(cfg, n_steps):
+    """Stream oracle of block 0 after the first n_steps steps of cfg."""
+    orc = StreamOracle(cfg.patches_per_frame, cfg.special_per_frame, cfg.scale_frames,
+                       cfg.sliding_window)
+    for s, nf in enumerate(workloads.step_schedule(cfg)[:n_steps]):
+        q, k, v = [t.double().numpy() for t in workloads.gen_step_qkv(cfg, 0, s, nf)]
+        orc.commit({0: (k, v)}, nf)
+    return orc
+
+
+def test_skip_append_equals_append_before_the_window_fills():
+    """While nothing is evicted, attending over the cache plus the frame's own
+    rows is attention over the same key multiset as appending the frame (in
+    another order), so both oracle paths must agree."""
+    cfg = workloads.get_config(0)               # scale 2, window 4: 6 frames before eviction
+    for n_steps in (1, 2):                      # F = 3, 4 accepted frames
+        orc = _tiny_oracle_after(cfg, n_steps)
+        assert orc.F + 1 <= cfg.scale_frames + cfg.sliding_window
+        q, k, v = [t.double().numpy() for t in workloads.gen_step_qkv(cfg, 0, 50 + n_steps, 1)]
+        skip = orc.skip_append_outputs(0, q, k, v)
+        app = orc.step_outputs(0, q, k, v)
+        assert np.abs(skip - app).max() <= 1e-12
+        assert orc.F == 3 + (n_steps - 1)       # unchanged by either call
+
+
+def test_skip_append_vs_brute_with_full_window():
+    """Window full: the frame sees the brute-force visible slots of F frames
+    (the oldest window frame still there, no eviction) plus its own tokens."""
+    cfg = workloads.get_config(0)
+    P, S, T = cfg.patches_per_frame, cfg.special_per_frame, cfg.tokens_per_frame
+    sched = workloads.step_schedule(cfg)[:6]
+    orc = _tiny_oracle_after(cfg, len(sched))
+    assert orc.F == 8 and orc.F > cfg.scale_frames + cfg.sliding_window
+    slots = brute.simulate_visible_slots(sched, P, S, cfg.scale_frames, cfg.sliding_window)[-1]
+    q, k, v = [t.double().numpy() for t in workloads.gen_step_qkv(cfg, 0, 77, 1)]
+    got = orc.skip_append_outputs(0, q, k, v, rows=np.array([0, T - 1]), heads=[1])
+    for out_row, r in zip(got, (0, T - 1)):
+        keys, vals = [], []
+        for (f, t) in sorted(slots):
+            kk, vv = orc.history.get(0, f)
+            keys.append(kk[t, 1]); vals.append(vv[t, 1])
+        for t in range(T):
+            keys.append(k[t, 1]); vals.append(v[t, 1])
+        ref = brute.scalar_attention(q[r, 1], keys, vals)
+        assert np.abs(out_row[0] - np.array(ref)).max() <= 1e-12
+
+
 def test_paged_equals_dense_over_mirror_pools():
     """Mirror host pools filled through the reference allocator's write map:
     walking them through its visible table reproduces the rule-derived rows
