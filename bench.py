@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--variant-steps", type=int, default=100,
                     help="timed steps of the same workload in fp16 (reported under 'variants')")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--batch-streams", type=int, default=4,
+                    help="independent streams of the batched-launch variant")
+    ap.add_argument("--batch-steps", type=int, default=30)
     ap.add_argument("--skip-steps", type=int, default=50,
                     help="skip-append frames timed after the run (reported under 'variants')")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -288,6 +291,67 @@ def measure_stream(cfg, dev, steps, warmup, splits_req=0, keep=False, skip_steps
         cache.close()
     return res
 
+def measure_batch(cfg, dev, n_streams, steps, splits_req=0, n_sets=2):
+    """n_streams independent streams of ``cfg`` (distinct seeds), each filled
+    to a full window, then ``steps`` frame steps in which every block runs as
+    one batched launch over all streams (lbm_run_batch).  Returns aggregate
+    frames/s and the attention TFLOP/s of the batched launches."""
+    import torch
+
+    import paged_kv_cache_312_amd as lbm
+    import workloads
+
+    B, H, D, T = cfg.num_blocks, cfg.num_heads, cfg.head_dim, cfg.tokens_per_frame
+    cfgs = [cfg.replace(base_seed=100 + i) for i in range(n_streams)]
+    caches = [lbm.PagedKVCache(lbm.make_config(**workloads.lbm_config_fields(c, num_splits=splits_req)), dev)
+              for c in cfgs]
+    init = [[workloads.gen_step_qkv(c, b, 0, c.initial_frames, dev) for b in range(B)] for c in cfgs]
+    sets = [[[workloads.gen_step_qkv(c, b, 1 + i, 1, dev) for b in range(B)] for i in range(n_sets)]
+            for c in cfgs]
+    outs = [[torch.empty((T, H, D), dtype=caches[0].dtype, device=dev) for _ in range(B)]
+            for _ in range(n_streams)]
+    stream = torch.cuda.current_stream()
+
+    def append_all(si, inputs, nq):
+        for b in range(B):
+            caches[si].append_frame(b, inputs[b][1], inputs[b][2])
+            if b == 0:
+                caches[si].evict_frames()
+                caches[si].plan(nq)
+
+    for si in range(n_streams):                       # fill: appends only
+        append_all(si, init[si], cfg.initial_frames * T)
+        for f in range(cfg.scale_frames + cfg.sliding_window - cfg.initial_frames):
+            append_all(si, sets[si][f % n_sets], T)
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in range(B)] for _ in range(steps)]
+    flops = 0.0
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for b in range(B):
+            for si in range(n_streams):
+                x = sets[si][i % n_sets][b]
+                caches[si].append_frame(b, x[1], x[2])
+                if b == 0:
+                    caches[si].evict_frames()
+                    caches[si].plan(T)
+            ev[i][b][0].record(stream)
+            lbm.PagedKVCache.run_batch(caches, b, [sets[si][i % n_sets][b][0]
+                                                   for si in range(n_streams)],
+                                       [outs[si][b] for si in range(n_streams)])
+            ev[i][b][1].record(stream)
+        flops += sum(B * 4.0 * T * c.get_plan()[0] * H * D for c in caches)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    attn_ms = sum(e0.elapsed_time(e1) for row in ev for e0, e1 in row)
+    F = caches[0].stats()["frame_count"]
+    for c in caches:
+        c.close()
+    return {"fps": n_streams * steps / elapsed, "tflops": flops / (attn_ms * 1e-3) / 1e12,
+            "avg_launch_ms": attn_ms / (steps * B), "F_last": F}
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -366,6 +430,15 @@ def main():
             "attention_tflops": round(v["tflops"], 2),
             "frac": round(v["tflops"] / PEAK_FP16_TFLOPS, 4), "peak": PEAK_FP16_TFLOPS,
             "avg_launch_ms": round(v["avg_launch_ms"], 4), "key_splits": v["splits"]}
+
+    if not args.no_variants and args.batch_streams > 1:
+        bt = measure_batch(cfg, dev, args.batch_streams, args.batch_steps, args.splits)
+        result.setdefault("variants", {})[f"batch{args.batch_streams}_bf16"] = {
+            "value": round(bt["fps"], 3), "unit": "frames/s (all streams)",
+            "streams": args.batch_streams, "steps": args.batch_steps,
+            "attention_tflops": round(bt["tflops"], 2),
+            "frac": round(bt["tflops"] / PEAK_BF16_TFLOPS, 4), "peak": PEAK_BF16_TFLOPS,
+            "avg_launch_ms": round(bt["avg_launch_ms"], 4)}
 
     if args.calibrate_copy:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)

@@ -204,6 +204,24 @@ lbm_status lbm_plan_transient(lbm_cache* cache, int32_t num_q_tokens, int32_t nu
 lbm_status lbm_run_transient(lbm_cache* cache, int32_t block_idx, const void* q, const void* k,
                              const void* v, void* out, int32_t num_q_tokens, void* hip_stream);
 
+/* Most streams in one batched run. */
+#define LBM_MAX_BATCH 8
+
+/* Batched run: block block_idx of n independent streams (caches), 1..LBM_MAX_BATCH, in one
+ * attention launch (and one merge launch per split stream) -- the pages'
+ * kernel is a batch prefill over the pages of several requests ([P1]
+ * "FlashInfer Paged-Kernel Integration": BatchPrefillWithPagedKVCacheWrapper).
+ * Each cache must hold a current plan made by lbm_plan (not a skip-append
+ * plan); q[i], out[i]: device [that plan's num_q_tokens, H, D].  All caches
+ * share num_heads, head_dim and dtype; they may differ in page sizes, frames
+ * and key lengths.  The key-range split count is chosen for the combined work
+ * (one count for the launch).  Results equal lbm_run of each cache with that
+ * split count.  Errors: INVALID_ARG (n, null or misaligned pointers, mismatched
+ * caches, a cache listed twice -- its workspace holds one stream's partials),
+ * BAD_STATE (as for lbm_run, per cache). */
+lbm_status lbm_run_batch(lbm_cache* const* caches, int32_t n, int32_t block_idx,
+                         const void* const* q, void* const* out, void* hip_stream);
+
 /* Stateless paged attention over caller-given tables (device int32 arrays):
  * the visible keys are the n_patch_pages patch pages listed in patch_ids
  * (each P tokens) followed by the first n_special_tokens tokens of the

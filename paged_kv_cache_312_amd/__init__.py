@@ -19,6 +19,7 @@ __all__ = [
     "lbm_query_sizes", "lbm_cache_create", "lbm_cache_destroy", "lbm_cache_reset",
     "lbm_cache_seed_free_lists", "lbm_append_frame", "lbm_evict_frames",
     "lbm_rollback_last_frame", "lbm_plan", "lbm_run", "lbm_plan_transient", "lbm_run_transient",
+    "lbm_run_batch", "MAX_BATCH",
     "lbm_paged_attention", "lbm_get_stats",
     "lbm_dump_state", "lbm_get_plan", "lbm_plan_num_splits", "lbm_last_error",
     "PagedKVCache", "CoreBookkeeping",
@@ -130,6 +131,17 @@ def lbm_run_transient(handle: int, block_idx: int, q: int, k: int, v: int, out: 
     _ck(lib().lbm_run_transient(c_void_p(handle), block_idx, c_void_p(q), c_void_p(k),
                                 c_void_p(v), c_void_p(out), num_q_tokens, c_void_p(stream)),
         "lbm_run_transient")
+
+
+MAX_BATCH = 8
+
+
+def lbm_run_batch(handles: List[int], block_idx: int, qs: List[int], outs: List[int],
+                  stream: int) -> None:
+    n = len(handles)
+    arr = lambda xs: (c_void_p * max(n, 1))(*[c_void_p(x) for x in xs])
+    _ck(lib().lbm_run_batch(arr(handles), n, block_idx, arr(qs), arr(outs), c_void_p(stream)),
+        "lbm_run_batch")
 
 
 def lbm_paged_attention(cfg: LbmConfig, q: int, out: int, num_q_tokens: int, patch_pool: int,
@@ -274,6 +286,19 @@ class PagedKVCache:
         lbm_run_transient(self.handle, block_idx, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                           out.data_ptr(), q.shape[0], self._stream(stream))
         return out
+
+    @staticmethod
+    def run_batch(caches: List["PagedKVCache"], block_idx: int, qs, outs=None, stream=None):
+        """Block ``block_idx`` of several caches (independent streams, each
+        planned) in one batched launch; returns the outputs."""
+        if outs is None:
+            outs = [c.torch.empty_like(q) for c, q in zip(caches, qs)]
+        for c, q, o in zip(caches, qs, outs):
+            c._check_tensor(q)
+            c._check_tensor(o, q.shape[0])
+        lbm_run_batch([c.handle for c in caches], block_idx, [q.data_ptr() for q in qs],
+                      [o.data_ptr() for o in outs], caches[0]._stream(stream))
+        return outs
 
     def reset(self) -> None:
         lbm_cache_reset(self.handle)

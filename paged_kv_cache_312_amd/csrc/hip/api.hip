@@ -9,7 +9,9 @@
 // which evict (commit) or rollback follows the runs ("How LingBot-Map Uses KV
 // Caching for Efficient Streaming Inference", section "Flow-Based Keyframe
 // Selection").
+#include <algorithm>
 #include <cmath>
+#include <cstdint>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -149,17 +151,36 @@ AttnArgs base_args(const lbm_config& c, const void* q, void* out, int32_t nq, co
   return a;
 }
 
-lbm_status launch_attention(const lbm_config& c, AttnArgs* a, int32_t splits, hipStream_t st) {
-  finish_attn_args(a, c.head_dim, splits);
-  const bool own = a->tr_start < a->kv_len;
-  hipError_t e = c.dtype == LBM_F32 ? launch_attn_f32(*a, c.head_dim, own, st)
-                                    : launch_attn16(*a, c.head_dim, c.dtype == LBM_F16, own, st);
+// One attention launch over n streams' args (1 <= n <= kMaxBatch; all with
+// c's head_dim and dtype, all with or all without own rows), then the merge
+// of every stream whose key range is split.
+lbm_status launch_attention_batch(const lbm_config& c, AttnArgs* as, int32_t n, int32_t splits,
+                                  hipStream_t st) {
+  BatchArgs b;
+  std::memset(&b, 0, sizeof(b));
+  b.n = n;
+  for (int32_t i = 0; i < n; ++i) {
+    finish_attn_args(&as[i], c.head_dim, splits);
+    b.s[i] = as[i];
+    b.item_start[i + 1] = b.item_start[i] + as[i].total_items;
+  }
+  b.total_items = b.item_start[n];
+  b.items_per_xcd = (b.total_items + 7) / 8;
+  const bool own = as[0].tr_start < as[0].kv_len;
+  hipError_t e = c.dtype == LBM_F32 ? launch_attn_f32(b, c.head_dim, own, st)
+                                    : launch_attn16(b, c.head_dim, c.dtype == LBM_F16, own, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
-  if (a->num_splits > 1) {
-    e = launch_merge(*a, c.head_dim, c.dtype, st);
-    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  for (int32_t i = 0; i < n; ++i) {
+    if (as[i].num_splits > 1) {
+      e = launch_merge(as[i], c.head_dim, c.dtype, st);
+      if (e != hipSuccess) return hip_fail(e, "merge launch");
+    }
   }
   return LBM_OK;
+}
+
+lbm_status launch_attention(const lbm_config& c, AttnArgs* a, int32_t splits, hipStream_t st) {
+  return launch_attention_batch(c, a, 1, splits, st);
 }
 
 }  // namespace
@@ -478,6 +499,53 @@ lbm_status lbm_run_transient(lbm_cache* c, int32_t block_idx, const void* q, con
   a.tk = k;
   a.tv = v;
   return launch_attention(c->cfg, &a, c->plan_splits, static_cast<hipStream_t>(hip_stream));
+}
+
+lbm_status lbm_run_batch(lbm_cache* const* caches, int32_t n, int32_t block_idx,
+                         const void* const* q, void* const* out, void* hip_stream) {
+  clear_error();
+  if (!caches || !q || !out) return fail(LBM_ERR_INVALID_ARG, "caches/q/out is null");
+  if (n < 1 || n > kMaxBatch) return fail(LBM_ERR_INVALID_ARG, "n %d outside 1..%d", n, kMaxBatch);
+  AttnArgs as[kMaxBatch];
+  int64_t rows = 0;
+  int32_t kv_max = 0, cap = kSplitMax;
+  const lbm_cache* c0 = caches[0];
+  for (int32_t i = 0; i < n; ++i) {
+    lbm_cache* c = caches[i];
+    lbm_status st = check_cache(c);
+    if (st != LBM_OK) return st;
+    for (int32_t j = 0; j < i; ++j)   // each cache's split partials live in its own workspace
+      if (caches[j] == c) return fail(LBM_ERR_INVALID_ARG, "cache %d appears twice", i);
+    if (c->cfg.num_heads != c0->cfg.num_heads || c->cfg.head_dim != c0->cfg.head_dim ||
+        c->cfg.dtype != c0->cfg.dtype)
+      return fail(LBM_ERR_INVALID_ARG, "cache %d: heads, head_dim or dtype differ from cache 0", i);
+    if (block_idx < 0 || block_idx >= c->cfg.num_blocks)
+      return fail(LBM_ERR_INVALID_ARG, "block_idx %d outside cache %d's 0..%d", block_idx, i,
+                  c->cfg.num_blocks - 1);
+    if (!q[i] || !out[i] || !aligned16(q[i]) || !aligned16(out[i]))
+      return fail(LBM_ERR_INVALID_ARG, "q/out %d null or not 16-byte aligned", i);
+    if (!c->plan_valid) return fail(LBM_ERR_BAD_STATE, "cache %d has no plan", i);
+    if (c->plan_epoch != c->bk.epoch()) return fail(LBM_ERR_BAD_STATE, "cache %d: stale plan", i);
+    if (c->plan_own > 0) return fail(LBM_ERR_BAD_STATE, "cache %d: a skip-append plan", i);
+    if (c->step_open && !c->appended[size_t(block_idx)])
+      return fail(LBM_ERR_BAD_STATE, "cache %d: block %d has not appended the open step", i,
+                  block_idx);
+    as[i] = base_args(c->cfg, q[i], out[i], c->plan_q, c->patch_pools[size_t(block_idx)],
+                      c->special_pools[size_t(block_idx)],
+                      reinterpret_cast<const uint32_t*>(c->workspace + c->ws.rowtab_off),
+                      c->workspace, c->ws);
+    as[i].kv_len = c->plan.kv_len;
+    as[i].tr_start = as[i].kv_len;
+    rows += int64_t(c->plan_q + kRowsPerGroup - 1) / kRowsPerGroup * kRowsPerGroup;
+    kv_max = std::max(kv_max, c->plan.kv_len);
+    cap = std::min(cap, split_capacity(c->ws, c->plan_q));
+  }
+  // one split count for the whole launch, chosen for the combined work
+  int32_t ns = choose_splits(int32_t(std::min<int64_t>(rows, INT32_MAX)), kv_max,
+                             c0->cfg.num_heads, c0->num_cu, c0->wg_per_cu, cap,
+                             c0->cfg.num_splits);
+  if (ns < 1) ns = 1;
+  return launch_attention_batch(c0->cfg, as, n, ns, static_cast<hipStream_t>(hip_stream));
 }
 
 lbm_status lbm_paged_attention(const lbm_config* cfg, const void* q, void* out,

@@ -136,7 +136,7 @@ __device__ __forceinline__ V8 v_operand(const uint16_t* p0, const uint16_t* p1) 
 // one kernel per element type: attn_d64_kernel<__bf16> and attn_d64_kernel<_Float16>;
 // TR: a skip-append step, whose last keys are the frame's own rows
 template <typename T, bool TR>
-__global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b) {
   typedef typename Elt<T>::v8 h8;
   typedef typename Elt<T>::v2 h2;
   // Rings indexed by tile position x (x = 0 is the split's first tile): K
@@ -146,8 +146,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const AttnArgs a)
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[NST][TILE];
   __shared__ __attribute__((aligned(16))) uint32_t lds_code[NCODE][64];
 
-  const int32_t item = work_item(a, blockIdx.x);
-  if (item < 0) return;
+  int32_t sid;
+  const int32_t item = work_item(b, blockIdx.x, sid);
+  if (sid < 0) return;
+  const AttnArgs& a = b.s[sid];
   const int32_t qt = item % a.n_qt;
   const int32_t grp = item / a.n_qt;
   const int32_t head = grp / a.num_splits;
@@ -512,18 +514,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const AttnArgs a)
 
 }  // namespace
 
-hipError_t launch_attn16(const AttnArgs& a, int32_t head_dim, bool fp16, bool transient,
+hipError_t launch_attn16(const BatchArgs& b, int32_t head_dim, bool fp16, bool transient,
                          hipStream_t stream) {
   if (head_dim != 64) return hipErrorInvalidValue;
-  const dim3 grid(8 * a.items_per_xcd), block(kThreads);
+  const dim3 grid(8 * b.items_per_xcd), block(kThreads);
   if (fp16 && transient)
-    hipLaunchKernelGGL((attn_d64_kernel<_Float16, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_d64_kernel<_Float16, true>), grid, block, 0, stream, b);
   else if (fp16)
-    hipLaunchKernelGGL((attn_d64_kernel<_Float16, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_d64_kernel<_Float16, false>), grid, block, 0, stream, b);
   else if (transient)
-    hipLaunchKernelGGL((attn_d64_kernel<__bf16, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_d64_kernel<__bf16, true>), grid, block, 0, stream, b);
   else
-    hipLaunchKernelGGL((attn_d64_kernel<__bf16, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_d64_kernel<__bf16, false>), grid, block, 0, stream, b);
   return hipGetLastError();
 }
 

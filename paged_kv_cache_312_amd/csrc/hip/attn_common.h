@@ -22,10 +22,18 @@ constexpr int kThreads = 256;  // 4 wavefronts of 64, 32 query rows each
 
 // Work item of workgroup `blk`: consecutive items go to one XCD (workgroup i
 // runs on XCD i mod 8), so the query groups sharing one head's key range run
-// side by side on one L2.  Returns -1 for a padding workgroup.
-__device__ __forceinline__ int32_t work_item(const AttnArgs& a, int32_t blk) {
-  const int32_t item = (blk & 7) * a.items_per_xcd + (blk >> 3);
-  return item < a.total_items ? item : -1;
+// side by side on one L2.  Returns the item within its stream and sets
+// `stream`; stream -1 for a padding workgroup.
+__device__ __forceinline__ int32_t work_item(const BatchArgs& b, int32_t blk, int32_t& stream) {
+  const int32_t gi = (blk & 7) * b.items_per_xcd + (blk >> 3);
+  if (gi >= b.total_items) {
+    stream = -1;
+    return -1;
+  }
+  int32_t s = 0;
+  while (s + 1 < b.n && gi >= b.item_start[s + 1]) ++s;
+  stream = s;
+  return gi - b.item_start[s];
 }
 
 // K and V row addresses of the key whose row code is `code` (see RowtabArgs);

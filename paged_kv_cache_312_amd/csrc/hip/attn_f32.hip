@@ -17,7 +17,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // TR: a skip-append step, whose keys [tr_start, kv_len) are the frame's own rows
 template <int D, bool TR>
-__global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(kThreads) void attn_f32_kernel(const BatchArgs b) {
   constexpr int KS = D + 4;          // LDS row strides (floats)
   constexpr int VS = D + 8;
   constexpr int CPR = D / 4;         // 16-byte chunks per key row
@@ -28,8 +28,10 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float lds_k[2][64 * KS];
   __shared__ __attribute__((aligned(16))) float lds_v[2][64 * VS];
 
-  const int32_t item = work_item(a, blockIdx.x);
-  if (item < 0) return;
+  int32_t sid;
+  const int32_t item = work_item(b, blockIdx.x, sid);
+  if (sid < 0) return;
+  const AttnArgs& a = b.s[sid];
   const int32_t qt = item % a.n_qt;
   const int32_t grp = item / a.n_qt;
   const int32_t head = grp / a.num_splits;
@@ -207,16 +209,16 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnArgs a) {
 
 }  // namespace
 
-hipError_t launch_attn_f32(const AttnArgs& a, int32_t head_dim, bool transient, hipStream_t stream) {
-  const dim3 grid(8 * a.items_per_xcd), block(kThreads);
+hipError_t launch_attn_f32(const BatchArgs& b, int32_t head_dim, bool transient, hipStream_t stream) {
+  const dim3 grid(8 * b.items_per_xcd), block(kThreads);
   if (head_dim == 64 && transient)
-    hipLaunchKernelGGL((attn_f32_kernel<64, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_f32_kernel<64, true>), grid, block, 0, stream, b);
   else if (head_dim == 64)
-    hipLaunchKernelGGL((attn_f32_kernel<64, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_f32_kernel<64, false>), grid, block, 0, stream, b);
   else if (head_dim == 32 && transient)
-    hipLaunchKernelGGL((attn_f32_kernel<32, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_f32_kernel<32, true>), grid, block, 0, stream, b);
   else if (head_dim == 32)
-    hipLaunchKernelGGL((attn_f32_kernel<32, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_f32_kernel<32, false>), grid, block, 0, stream, b);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -73,14 +73,26 @@ struct AttnArgs {
   float scale_log2;           // log2(e) / sqrt(D)
 };
 
+// One attention launch over n independent streams (caches), n <= kMaxBatch:
+// the work items of stream s are [item_start[s], item_start[s+1]) of the
+// launch's item range, each stream's laid out as a single-stream launch's.
+constexpr int kMaxBatch = 8;
+struct BatchArgs {
+  int32_t n;
+  int32_t total_items;        // item_start[n]
+  int32_t items_per_xcd;      // ceil(total_items / 8)
+  int32_t item_start[kMaxBatch + 1];
+  AttnArgs s[kMaxBatch];
+};
+
 // Fill the split/grid fields of `a` for a launch (Tq, kv_len, splits known).
 void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits);
 
 // 16-bit inputs: bf16, or fp16 when `fp16`; `transient`: a skip-append step
 // (tr_start < kv_len)
-hipError_t launch_attn16(const AttnArgs& a, int32_t head_dim, bool fp16, bool transient,
+hipError_t launch_attn16(const BatchArgs& b, int32_t head_dim, bool fp16, bool transient,
                          hipStream_t stream);
-hipError_t launch_attn_f32(const AttnArgs& a, int32_t head_dim, bool transient, hipStream_t stream);
+hipError_t launch_attn_f32(const BatchArgs& b, int32_t head_dim, bool transient, hipStream_t stream);
 
 // Combine the key-range splits' partials into the output (after an attention
 // launch with num_splits > 1, on the same stream).
