@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const BatchArgs b) {
   int32_t sid;
   const int32_t item = work_item(b, blockIdx.x, sid);
   if (sid < 0) return;
-  const AttnArgs& a = b.s[sid];
+  const AttnArgs a = b.s[sid];  // a copy: values, not loads that a memory barrier would repeat
   const int32_t qt = item % a.n_qt;
   const int32_t grp = item / a.n_qt;
   const int32_t head = grp / a.num_splits;
