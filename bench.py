@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--variant-steps", type=int, default=100,
                     help="timed steps of the same workload in fp16 (reported under 'variants')")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--graph-steps", type=int, default=100,
+                    help="frame steps replayed as HIP graphs (reported under 'variants')")
     ap.add_argument("--batch-streams", type=int, default=4,
                     help="independent streams of the batched-launch variant")
     ap.add_argument("--batch-steps", type=int, default=30)
@@ -352,6 +354,65 @@ def measure_batch(cfg, dev, n_streams, steps, splits_req=0, n_sets=2):
             "avg_launch_ms": attn_ms / (steps * B), "F_last": F}
 
 
+def measure_graph(cfg, dev, steps, n_sets=N_INPUT_SETS):
+    """The stream of ``cfg`` filled to a full window with the individual
+    calls, then ``steps`` frame steps each replayed as one HIP graph (one graph
+    per resident input set, its outputs in fixed buffers).  Returns frames/s
+    and the host time to submit one step: through the graph, and through the
+    individual calls (append, evict, plan, run per block) for comparison."""
+    import statistics
+
+    import torch
+
+    import paged_kv_cache_312_amd as lbm
+    import workloads
+
+    B, H, D, T = cfg.num_blocks, cfg.num_heads, cfg.head_dim, cfg.tokens_per_frame
+    cache = lbm.PagedKVCache(lbm.make_config(**workloads.lbm_config_fields(cfg)), dev)
+    init = [workloads.gen_step_qkv(cfg, b, 0, cfg.initial_frames, dev) for b in range(B)]
+    sets = [[workloads.gen_step_qkv(cfg, b, 1 + i, 1, dev) for b in range(B)] for i in range(n_sets)]
+    outs = [torch.empty((T, H, D), dtype=cache.dtype, device=dev) for _ in range(B)]
+
+    def calls(inputs, nq):
+        for b in range(B):
+            q, k, v = inputs[b]
+            cache.append_frame(b, k, v)
+            if b == 0:
+                cache.evict_frames()
+                cache.plan(nq)
+            cache.run(b, q, outs[b])
+
+    calls(init, cfg.initial_frames * T)
+    for f in range(cfg.scale_frames + cfg.sliding_window - cfg.initial_frames):
+        calls(sets[f % n_sets], T)
+    graphs = [cache.capture_step(1, [x[1] for x in st], [x[2] for x in st], [x[0] for x in st],
+                                 outs) for st in sets]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % n_sets].launch()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    host_graph, host_calls = [], []
+    for i in range(5):
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        graphs[i % n_sets].launch()
+        host_graph.append(time.perf_counter() - t1)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        calls(sets[i % n_sets], T)
+        host_calls.append(time.perf_counter() - t1)
+    torch.cuda.synchronize()
+    ns = graphs[0].num_splits()
+    for g in graphs:
+        g.close()
+    cache.close()
+    return {"fps": steps / elapsed, "ms_per_step": elapsed * 1e3 / steps,
+            "host_submit_ms_graph": statistics.median(host_graph) * 1e3,
+            "host_submit_ms_calls": statistics.median(host_calls) * 1e3, "splits": ns}
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -430,6 +491,14 @@ def main():
             "attention_tflops": round(v["tflops"], 2),
             "frac": round(v["tflops"] / PEAK_FP16_TFLOPS, 4), "peak": PEAK_FP16_TFLOPS,
             "avg_launch_ms": round(v["avg_launch_ms"], 4), "key_splits": v["splits"]}
+
+    if not args.no_variants and args.graph_steps > 0:
+        gr = measure_graph(cfg, dev, args.graph_steps)
+        result.setdefault("variants", {})["graph_bf16"] = {
+            "value": round(gr["fps"], 3), "unit": "frames/s", "steps": args.graph_steps,
+            "ms_per_step": round(gr["ms_per_step"], 4), "key_splits": gr["splits"],
+            "host_submit_ms_graph": round(gr["host_submit_ms_graph"], 3),
+            "host_submit_ms_calls": round(gr["host_submit_ms_calls"], 3)}
 
     if not args.no_variants and args.batch_streams > 1:
         bt = measure_batch(cfg, dev, args.batch_streams, args.batch_steps, args.splits)

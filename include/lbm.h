@@ -222,6 +222,41 @@ lbm_status lbm_run_transient(lbm_cache* cache, int32_t block_idx, const void* q,
 lbm_status lbm_run_batch(lbm_cache* const* caches, int32_t n, int32_t block_idx,
                          const void* const* q, void* const* out, void* hip_stream);
 
+/* A whole frame step as one HIP graph ([P1] "Implementation Examples": the
+ * block compiles its operations into CUDA graphs).  lbm_graph_create captures,
+ * over fixed caller buffers -- per block b: k[b], v[b] (the step's num_frames
+ * frames, [num_frames*T, H, D]), q[b] and out[b] ([num_frames*T, H, D]) --
+ * one step: every block's append scatter, the row table, every block's
+ * attention (and merge), all reading the step's page tables and lengths from
+ * the workspace.  k, v, q, out: host arrays of num_blocks device pointers,
+ * 16-byte aligned; the buffers must stay valid while the graph lives.  The
+ * key-range split count is fixed at capture (cfg.num_splits, else the
+ * planner's choice for the full window); splits a step leaves without keys
+ * contribute nothing.  Destroy graphs before their cache.  Errors: INVALID_ARG,
+ * HIP. */
+typedef struct lbm_graph lbm_graph;
+lbm_status lbm_graph_create(lbm_cache* cache, int32_t num_frames, const void* const* k,
+                            const void* const* v, const void* const* q, void* const* out,
+                            lbm_graph** out_graph);
+
+/* One frame step through the graph: on the host, the bookkeeping of append
+ * (page reservation), eviction and the plan; then one graph launch on
+ * hip_stream that copies the step's tables and runs every block.  Results and
+ * cache state equal those of the call sequence append (every block), evict,
+ * plan, run (every block) with the graph's split count.  The caller fills
+ * k/v/q before the launch (in stream order) and reads out after it.  The host
+ * may run at most two steps ahead of the device (pinned staging in two
+ * slots).  Errors: OUT_OF_PAGES, BAD_STATE (a step open and not every block
+ * appended), HIP.  A HIP failure after the reservation leaves the
+ * bookkeeping a step ahead of the pools. */
+lbm_status lbm_graph_launch(lbm_graph* graph, void* hip_stream);
+
+/* The split count fixed at capture (0 for a null graph). */
+int32_t lbm_graph_num_splits(const lbm_graph* graph);
+
+/* Waits for the graph's pending launches, then frees it. */
+void lbm_graph_destroy(lbm_graph* graph);
+
 /* Stateless paged attention over caller-given tables (device int32 arrays):
  * the visible keys are the n_patch_pages patch pages listed in patch_ids
  * (each P tokens) followed by the first n_special_tokens tokens of the

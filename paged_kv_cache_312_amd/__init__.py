@@ -19,7 +19,8 @@ __all__ = [
     "lbm_query_sizes", "lbm_cache_create", "lbm_cache_destroy", "lbm_cache_reset",
     "lbm_cache_seed_free_lists", "lbm_append_frame", "lbm_evict_frames",
     "lbm_rollback_last_frame", "lbm_plan", "lbm_run", "lbm_plan_transient", "lbm_run_transient",
-    "lbm_run_batch", "MAX_BATCH",
+    "lbm_run_batch", "MAX_BATCH", "lbm_graph_create", "lbm_graph_launch", "lbm_graph_destroy",
+    "lbm_graph_num_splits", "StepGraph",
     "lbm_paged_attention", "lbm_get_stats",
     "lbm_dump_state", "lbm_get_plan", "lbm_plan_num_splits", "lbm_last_error",
     "PagedKVCache", "CoreBookkeeping",
@@ -142,6 +143,27 @@ def lbm_run_batch(handles: List[int], block_idx: int, qs: List[int], outs: List[
     arr = lambda xs: (c_void_p * max(n, 1))(*[c_void_p(x) for x in xs])
     _ck(lib().lbm_run_batch(arr(handles), n, block_idx, arr(qs), arr(outs), c_void_p(stream)),
         "lbm_run_batch")
+
+
+def lbm_graph_create(handle: int, num_frames: int, ks: List[int], vs: List[int], qs: List[int],
+                     outs: List[int]) -> int:
+    arr = lambda xs: (c_void_p * len(xs))(*[c_void_p(x) for x in xs])
+    g = c_void_p()
+    _ck(lib().lbm_graph_create(c_void_p(handle), num_frames, arr(ks), arr(vs), arr(qs), arr(outs),
+                               ctypes.byref(g)), "lbm_graph_create")
+    return g.value
+
+
+def lbm_graph_launch(graph: int, stream: int) -> None:
+    _ck(lib().lbm_graph_launch(c_void_p(graph), c_void_p(stream)), "lbm_graph_launch")
+
+
+def lbm_graph_num_splits(graph: int) -> int:
+    return lib().lbm_graph_num_splits(c_void_p(graph))
+
+
+def lbm_graph_destroy(graph: int) -> None:
+    lib().lbm_graph_destroy(c_void_p(graph))
 
 
 def lbm_paged_attention(cfg: LbmConfig, q: int, out: int, num_q_tokens: int, patch_pool: int,
@@ -287,6 +309,11 @@ class PagedKVCache:
                           out.data_ptr(), q.shape[0], self._stream(stream))
         return out
 
+    def capture_step(self, num_frames: int, ks, vs, qs, outs) -> "StepGraph":
+        """Capture a whole frame step over fixed per-block buffers (k, v, q,
+        out lists, one tensor per block) as a HIP graph."""
+        return StepGraph(self, num_frames, ks, vs, qs, outs)
+
     @staticmethod
     def run_batch(caches: List["PagedKVCache"], block_idx: int, qs, outs=None, stream=None):
         """Block ``block_idx`` of several caches (independent streams, each
@@ -388,3 +415,39 @@ class CoreBookkeeping:
     def choose_splits(num_q_tokens, kv_len, num_heads, num_cu, wg_per_cu, split_cap, forced=0):
         return core_lib().lbmcore_choose_splits(num_q_tokens, kv_len, num_heads, num_cu,
                                                 wg_per_cu, split_cap, forced)
+
+
+class StepGraph:
+    """A frame step replayed as one HIP graph over fixed buffers: fill the
+    buffers, then ``launch()`` does append, evict, plan and every block's
+    attention (outputs in the ``outs`` tensors)."""
+
+    def __init__(self, cache: PagedKVCache, num_frames: int, ks, vs, qs, outs):
+        T = cache.cfg.patches_per_frame + cache.cfg.special_per_frame
+        B = cache.cfg.num_blocks
+        if not (len(ks) == len(vs) == len(qs) == len(outs) == B):
+            raise ValueError(f"one k, v, q and out tensor per block ({B})")
+        for t in list(ks) + list(vs) + list(qs) + list(outs):
+            cache._check_tensor(t, num_frames * T)
+        self.cache = cache
+        self.buffers = (list(ks), list(vs), list(qs), list(outs))   # kept alive
+        self.handle = lbm_graph_create(cache.handle, num_frames, [t.data_ptr() for t in ks],
+                                       [t.data_ptr() for t in vs], [t.data_ptr() for t in qs],
+                                       [t.data_ptr() for t in outs])
+
+    def num_splits(self) -> int:
+        return lbm_graph_num_splits(self.handle)
+
+    def launch(self, stream=None) -> None:
+        lbm_graph_launch(self.handle, self.cache._stream(stream))
+
+    def close(self) -> None:
+        if self.handle:
+            lbm_graph_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

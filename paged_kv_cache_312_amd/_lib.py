@@ -61,6 +61,11 @@ LBM_FUNCS = {
     "lbm_plan_transient": (c_int32, [c_void_p, c_int32, c_int32, c_void_p]),
     "lbm_run_batch": (c_int32, [POINTER(c_void_p), c_int32, c_int32, POINTER(c_void_p),
                                 POINTER(c_void_p), c_void_p]),
+    "lbm_graph_create": (c_int32, [c_void_p, c_int32, POINTER(c_void_p), POINTER(c_void_p),
+                                   POINTER(c_void_p), POINTER(c_void_p), POINTER(c_void_p)]),
+    "lbm_graph_launch": (c_int32, [c_void_p, c_void_p]),
+    "lbm_graph_num_splits": (c_int32, [c_void_p]),
+    "lbm_graph_destroy": (None, [c_void_p]),
     "lbm_run_transient": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_int32, c_void_p]),
     "lbm_paged_attention": (c_int32, [POINTER(LbmConfig), c_void_p, c_void_p, c_int32, c_void_p,

@@ -336,6 +336,8 @@ int32_t choose_splits(int32_t num_q_tokens, int32_t kv_len, int32_t num_heads, i
 WorkspaceLayout workspace_layout(const lbm_config& c) {
   WorkspaceLayout w;
   size_t off = 0;
+  w.desc_off = off;
+  off = align_up(off + sizeof(StepDesc), 256);
   w.patch_ids_off = off;
   off = align_up(off + sizeof(int32_t) * size_t(std::max(1, c.scale_frames + c.sliding_window)), 256);
   w.special_ids_off = off;

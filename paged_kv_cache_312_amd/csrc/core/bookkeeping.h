@@ -120,7 +120,24 @@ int32_t choose_splits(int32_t num_q_tokens, int32_t kv_len, int32_t num_heads, i
                       int32_t wg_per_cu, int32_t split_cap, int32_t forced);
 
 // Workspace layout (byte offsets from the workspace base).
+// Per-step values of a frame step that graph-replayed launches read from
+// device memory (their own arguments stay those of the capture): the host
+// writes it, with the step's page tables, into pinned staging that the graph's
+// first node copies to the workspace.
+struct StepDesc {
+  int32_t kv_len = 0;           // visible keys
+  int32_t patch_tokens = 0;     // visible patch pages * P
+  int32_t n_tiles = 0;          // ceil(kv_len / 64)
+  int32_t tiles_per_split = 0;  // for the graph's split count (later splits may be empty)
+  int32_t st0 = 0;              // append: special tokens before the step
+  int32_t sp_first = 0;         // append: index of the page holding token st0
+  int32_t pad[2] = {};
+  int32_t patch_pages[kMaxStepFrames] = {};
+  int32_t spages[kMaxStepSpecialPages] = {};
+};
+
 struct WorkspaceLayout {
+  size_t desc_off = 0;        // StepDesc (graph-replayed steps)
   size_t patch_ids_off = 0;   // int32 [scale_frames + sliding_window]
   size_t special_ids_off = 0; // int32 [max_special_pages]
   size_t rowtab_off = 0;      // uint32 [rowtab_len]: per key position, the pool and row

@@ -90,6 +90,22 @@ struct lbm_cache {
   size_t staging_bytes = 0;
 };
 
+// A frame step captured as a HIP graph over fixed buffers (see lbm.h).  Two
+// instances of the same capture, each copying from its own pinned staging
+// buffer, let the host fill one while the other's copy may still be queued.
+struct lbm_graph {
+  lbm_cache* c = nullptr;
+  int32_t nf = 0, nq = 0, ns = 0;
+  size_t bytes = 0;                 // staging = workspace [desc_off, special ids end)
+  hipStream_t cap_stream = nullptr;
+  hipGraph_t graph[2] = {nullptr, nullptr};
+  hipGraphExec_t exec[2] = {nullptr, nullptr};
+  char* staging[2] = {nullptr, nullptr};
+  hipEvent_t done[2] = {nullptr, nullptr};
+  bool pending[2] = {false, false};
+  int next = 0;
+};
+
 namespace {
 
 lbm_status check_cache(const lbm_cache* c) {
@@ -618,6 +634,219 @@ lbm_status lbm_get_plan(const lbm_cache* c, int32_t* buf, int64_t cap, int64_t* 
   std::vector<int32_t> v;
   c->bk.plan_record(&v);
   return copy_record(v, buf, cap, len);
+}
+
+
+namespace {
+
+void graph_release(lbm_graph* g) {
+  for (int i = 0; i < 2; ++i) {
+    if (g->done[i]) {
+      if (g->pending[i]) (void)hipEventSynchronize(g->done[i]);
+      (void)hipEventDestroy(g->done[i]);
+    }
+    if (g->exec[i]) (void)hipGraphExecDestroy(g->exec[i]);
+    if (g->graph[i]) (void)hipGraphDestroy(g->graph[i]);
+    if (g->staging[i]) (void)hipHostFree(g->staging[i]);
+  }
+  if (g->cap_stream) (void)hipStreamDestroy(g->cap_stream);
+  delete g;
+}
+
+// Record one instance of the step on g->cap_stream: the copy of staging[i]
+// into the workspace, every block's append, the row table, every block's
+// attention (and merge); all per-step values are read from the copied
+// StepDesc.
+lbm_status graph_capture(lbm_graph* g, int i, const void* const* k, const void* const* v,
+                         const void* const* q, void* const* out) {
+  lbm_cache* c = g->c;
+  const lbm_config& cfg = c->cfg;
+  const StepDesc* desc = reinterpret_cast<const StepDesc*>(c->workspace + c->ws.desc_off);
+  hipError_t e = hipStreamBeginCapture(g->cap_stream, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return hip_fail(e, "graph capture begin");
+  lbm_status st = LBM_OK;
+  e = hipMemcpyAsync(c->workspace + c->ws.desc_off, g->staging[i], g->bytes,
+                     hipMemcpyHostToDevice, g->cap_stream);
+  if (e != hipSuccess) st = hip_fail(e, "graph table copy");
+  for (int32_t b = 0; st == LBM_OK && b < cfg.num_blocks; ++b) {
+    AppendArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.k = static_cast<const uint4*>(k[b]);
+    a.v = static_cast<const uint4*>(v[b]);
+    a.patch_pool = static_cast<uint4*>(c->patch_pools[size_t(b)]);
+    a.special_pool = static_cast<uint4*>(c->special_pools[size_t(b)]);
+    a.P = cfg.patches_per_frame;
+    a.S = cfg.special_per_frame;
+    a.T = a.P + a.S;
+    a.SPS = cfg.special_page_size;
+    a.rc = int32_t(size_t(cfg.num_heads) * cfg.head_dim * dtype_size(cfg.dtype) / 16);
+    a.desc = desc;
+    e = launch_append(a, g->nf, g->cap_stream);
+    if (e != hipSuccess) st = hip_fail(e, "graph append");
+  }
+  if (st == LBM_OK) {
+    RowtabArgs r;
+    std::memset(&r, 0, sizeof(r));
+    r.patch_ids = reinterpret_cast<const int32_t*>(c->workspace + c->ws.patch_ids_off);
+    r.special_ids = reinterpret_cast<const int32_t*>(c->workspace + c->ws.special_ids_off);
+    r.rowtab = reinterpret_cast<uint32_t*>(c->workspace + c->ws.rowtab_off);
+    r.P = cfg.patches_per_frame;
+    r.SPS = cfg.special_page_size;
+    r.n_pos = c->ws.rowtab_len;
+    r.row_bytes = int32_t(size_t(cfg.num_heads) * cfg.head_dim * dtype_size(cfg.dtype));
+    r.inv_P = 1.0f / float(r.P);
+    r.inv_SPS = 1.0f / float(r.SPS);
+    r.desc = desc;
+    e = launch_rowtab(r, g->cap_stream);
+    if (e != hipSuccess) st = hip_fail(e, "graph row table");
+  }
+  for (int32_t b = 0; st == LBM_OK && b < cfg.num_blocks; ++b) {
+    AttnArgs a = base_args(cfg, q[b], out[b], g->nq, c->patch_pools[size_t(b)],
+                           c->special_pools[size_t(b)],
+                           reinterpret_cast<const uint32_t*>(c->workspace + c->ws.rowtab_off),
+                           c->workspace, c->ws);
+    // launch shape for exactly g->ns splits; the kernels take the step's key
+    // range from the descriptor
+    a.kv_len = g->ns * kKeysPerTile;
+    a.tr_start = a.kv_len;
+    a.desc = desc;
+    st = launch_attention(cfg, &a, g->ns, g->cap_stream);
+  }
+  hipGraph_t graph = nullptr;
+  e = hipStreamEndCapture(g->cap_stream, &graph);
+  if (st != LBM_OK) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return st;
+  }
+  if (e != hipSuccess) return hip_fail(e, "graph capture end");
+  g->graph[i] = graph;
+  e = hipGraphInstantiate(&g->exec[i], graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) return hip_fail(e, "graph instantiate");
+  return LBM_OK;
+}
+
+}  // namespace
+
+lbm_status lbm_graph_create(lbm_cache* c, int32_t num_frames, const void* const* k,
+                            const void* const* v, const void* const* q, void* const* out,
+                            lbm_graph** out_graph) {
+  clear_error();
+  lbm_status st = check_cache(c);
+  if (st != LBM_OK) return st;
+  if (!out_graph || !k || !v || !q || !out)
+    return fail(LBM_ERR_INVALID_ARG, "k/v/q/out or out_graph is null");
+  if (num_frames < 1 || num_frames > c->cfg.max_frames_per_step)
+    return fail(LBM_ERR_INVALID_ARG, "num_frames %d outside 1..%d", num_frames,
+                c->cfg.max_frames_per_step);
+  const int32_t T = c->cfg.patches_per_frame + c->cfg.special_per_frame;
+  const int32_t nq = num_frames * T;
+  if (nq > c->cfg.max_q_tokens)
+    return fail(LBM_ERR_INVALID_ARG, "%d query rows exceed max_q_tokens %d", nq,
+                c->cfg.max_q_tokens);
+  for (int32_t b = 0; b < c->cfg.num_blocks; ++b)
+    if (!k[b] || !v[b] || !q[b] || !out[b] || !aligned16(k[b]) || !aligned16(v[b]) ||
+        !aligned16(q[b]) || !aligned16(out[b]))
+      return fail(LBM_ERR_INVALID_ARG, "block %d: k/v/q/out null or not 16-byte aligned", b);
+  lbm_graph* g = new (std::nothrow) lbm_graph();
+  if (!g) return fail(LBM_ERR_INVALID_ARG, "out of host memory");
+  g->c = c;
+  g->nf = num_frames;
+  g->nq = nq;
+  // split count for the steady state: the full window of patch pages and
+  // the special tokens so far
+  const int64_t kv_est = int64_t(c->cfg.scale_frames + c->cfg.sliding_window) *
+                             c->cfg.patches_per_frame + c->bk.plan_info().special_tokens + nq;
+  g->ns = choose_splits(nq, int32_t(std::min<int64_t>(kv_est, kMaxKvLen - 1)), c->cfg.num_heads,
+                        c->num_cu, c->wg_per_cu, split_capacity(c->ws, nq), c->cfg.num_splits);
+  if (g->ns < 1) g->ns = 1;
+  g->bytes = c->ws.special_ids_off + sizeof(int32_t) * size_t(std::max(1, c->cfg.max_special_pages)) -
+             c->ws.desc_off;
+  hipError_t e = hipStreamCreateWithFlags(&g->cap_stream, hipStreamNonBlocking);
+  for (int i = 0; e == hipSuccess && i < 2; ++i) {
+    e = hipHostMalloc(reinterpret_cast<void**>(&g->staging[i]), g->bytes, hipHostMallocDefault);
+    if (e == hipSuccess) {
+      std::memset(g->staging[i], 0, g->bytes);
+      e = hipEventCreateWithFlags(&g->done[i], hipEventDisableTiming);
+    }
+  }
+  if (e != hipSuccess) {
+    graph_release(g);
+    return hip_fail(e, "graph resources");
+  }
+  for (int i = 0; i < 2; ++i) {
+    st = graph_capture(g, i, k, v, q, out);
+    if (st != LBM_OK) {
+      graph_release(g);
+      return st;
+    }
+  }
+  *out_graph = g;
+  return LBM_OK;
+}
+
+lbm_status lbm_graph_launch(lbm_graph* g, void* hip_stream) {
+  clear_error();
+  if (!g) return fail(LBM_ERR_INVALID_ARG, "graph is null");
+  lbm_cache* c = g->c;
+  if (c->step_open) {
+    for (int32_t b = 0; b < c->cfg.num_blocks; ++b)
+      if (!c->appended[size_t(b)])
+        return fail(LBM_ERR_BAD_STATE, "block %d has not appended the open step", b);
+  }
+  const int i = g->next;
+  if (g->pending[i]) {
+    const hipError_t e = hipEventSynchronize(g->done[i]);
+    if (e != hipSuccess) return hip_fail(e, "graph staging wait");
+    g->pending[i] = false;
+  }
+  lbm_status st = c->bk.reserve(g->nf);
+  if (st != LBM_OK) return st;
+  std::vector<int32_t> evicted;
+  st = c->bk.evict(&evicted);
+  if (st != LBM_OK) return st;
+  const PlanInfo p = c->bk.plan_info();
+  const WriteMap& wm = c->bk.write_map();
+  StepDesc d;
+  d.kv_len = p.kv_len;
+  d.patch_tokens = p.patch_tokens;
+  d.n_tiles = (p.kv_len + kKeysPerTile - 1) / kKeysPerTile;
+  d.tiles_per_split = (d.n_tiles + g->ns - 1) / g->ns;
+  d.st0 = wm.st0;
+  d.sp_first = wm.sp_first;
+  for (int32_t f = 0; f < wm.nf; ++f) d.patch_pages[f] = wm.patch_pages[f];
+  for (int32_t j = 0; j < wm.n_sp; ++j) d.spages[j] = wm.spages[j];
+  char* stg = g->staging[i];
+  std::memcpy(stg, &d, sizeof(d));
+  std::vector<int32_t> pp;
+  c->bk.visible_patch_pages(&pp);
+  std::memcpy(stg + (c->ws.patch_ids_off - c->ws.desc_off), pp.data(), sizeof(int32_t) * pp.size());
+  const std::vector<int32_t>& sp = c->bk.special_pages();
+  if (!sp.empty())
+    std::memcpy(stg + (c->ws.special_ids_off - c->ws.desc_off), sp.data(),
+                sizeof(int32_t) * sp.size());
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = hipGraphLaunch(g->exec[i], s);
+  if (e == hipSuccess) e = hipEventRecord(g->done[i], s);
+  if (e != hipSuccess) return hip_fail(e, "graph launch");
+  g->pending[i] = true;
+  g->next = i ^ 1;
+  // the cache is left as after the call sequence append(all blocks), evict, plan
+  c->step_open = true;
+  c->step_nf = g->nf;
+  std::fill(c->appended.begin(), c->appended.end(), 1);
+  c->plan = p;
+  c->plan_q = g->nq;
+  c->plan_splits = g->ns;
+  c->plan_own = 0;
+  c->plan_epoch = c->bk.epoch();
+  c->plan_valid = true;
+  return LBM_OK;
+}
+
+int32_t lbm_graph_num_splits(const lbm_graph* g) { return g ? g->ns : 0; }
+
+void lbm_graph_destroy(lbm_graph* g) {
+  if (g) graph_release(g);
 }
 
 }  // extern "C"

@@ -20,15 +20,19 @@ __global__ void append_scatter_kernel(const AppendArgs a) {
   const int32_t f = row / a.T;
   const int32_t t = row - f * a.T;
   const uint4* src = (kv ? a.v : a.k) + size_t(row) * a.rc;
+  const int32_t* patch_pages = a.desc ? a.desc->patch_pages : a.patch_pages;
+  const int32_t* spages = a.desc ? a.desc->spages : a.spages;
   uint4* dst;
   if (t < a.P) {
-    const size_t page = size_t(a.patch_pages[f]);
+    const size_t page = size_t(patch_pages[f]);
     dst = a.patch_pool + ((page * 2 + kv) * a.P + t) * size_t(a.rc);
   } else {
-    const int32_t g = a.st0 + f * a.S + (t - a.P);  // special token index in the stream
+    const int32_t st0 = a.desc ? a.desc->st0 : a.st0;
+    const int32_t sp_first = a.desc ? a.desc->sp_first : a.sp_first;
+    const int32_t g = st0 + f * a.S + (t - a.P);  // special token index in the stream
     const int32_t pi = g / a.SPS;
     const int32_t slot = g - pi * a.SPS;
-    const size_t page = size_t(a.spages[pi - a.sp_first]);
+    const size_t page = size_t(spages[pi - sp_first]);
     dst = a.special_pool + ((page * 2 + kv) * a.SPS + slot) * size_t(a.rc);
   }
   for (int32_t c = threadIdx.x; c < a.rc; c += blockDim.x) dst[c] = src[c];

@@ -149,7 +149,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   int32_t sid;
   const int32_t item = work_item(b, blockIdx.x, sid);
   if (sid < 0) return;
-  const AttnArgs a = b.s[sid];  // a copy: values, not loads that a memory barrier would repeat
+  AttnArgs a = b.s[sid];  // a copy: values, not loads that a memory barrier would repeat
+  if (a.desc) {
+    a.kv_len = a.desc->kv_len;
+    a.n_tiles = a.desc->n_tiles;
+    a.tiles_per_split = a.desc->tiles_per_split;
+    a.tr_start = a.kv_len;
+  }
   const int32_t qt = item % a.n_qt;
   const int32_t grp = item / a.n_qt;
   const int32_t head = grp / a.num_splits;
@@ -161,6 +167,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   const int32_t HD = a.H * D;
   const int32_t t_begin = split * a.tiles_per_split;
   const int32_t t_end = min(a.n_tiles, t_begin + a.tiles_per_split);
+  if (t_end <= t_begin) {
+    // a split left without keys (graph-replayed steps keep the capture's split
+    // count): an empty partial, weight 0 in the merge
+    const int32_t qrow0 = qt * 128 + wave * 32 + l32;
+    if (qrow0 < a.Tq) {
+      const size_t rh = (size_t(split) * a.rows_pad + qrow0) * a.H + head;
+      float* po = a.part_o + rh * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<float4*>(po + db * 32 + 8 * i + 4 * hh) = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + rh * 2) = make_float2(-INFINITY, 0.f);
+    }
+    return;
+  }
 
   // Q as the B operand of S^T = K Q^T: row `qrow`, columns 16ks + 8hh .. +7,
   // pre-multiplied by log2(e)/sqrt(D) (rounded to T) so that the MFMA

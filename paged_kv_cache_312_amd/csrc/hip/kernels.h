@@ -22,6 +22,7 @@ struct AppendArgs {
   int32_t sp_first;        // index of the page holding token st0 in the special page list
   int32_t patch_pages[kMaxStepFrames];
   int32_t spages[kMaxStepSpecialPages];
+  const StepDesc* desc;    // graph-replayed step: st0, sp_first and the pages from here
 };
 
 hipError_t launch_append(const AppendArgs& a, int32_t nf, hipStream_t stream);
@@ -40,6 +41,8 @@ struct RowtabArgs {
   int32_t n_pos;              // n_tiles * 64
   int32_t row_bytes;          // H * D * element size
   float inv_P, inv_SPS;
+  const StepDesc* desc;       // graph-replayed step: kv_len, patch_tokens from here (the
+                              // grid covers the table's capacity)
 };
 
 hipError_t launch_rowtab(const RowtabArgs& a, hipStream_t stream);
@@ -64,6 +67,10 @@ struct AttnArgs {
   const void* tv;
   int32_t tr_start;
   int32_t row_bytes;          // H * D * element size
+  // Graph-replayed step: kv_len, n_tiles and tiles_per_split come from here
+  // (num_splits stays the capture's; splits left without keys write empty
+  // partials).
+  const StepDesc* desc;
   int32_t n_tiles;            // ceil(kv_len / 64)
   int32_t num_splits, tiles_per_split;
   int32_t n_qt;               // ceil(Tq / 128)

@@ -43,8 +43,13 @@ __device__ __forceinline__ uint32_t row_code(const RowtabArgs& a, int32_t j) {
   return uint32_t(row * a.row_bytes) | 0x80000000u;
 }
 
-__global__ void rowtab_kernel(const RowtabArgs a) {
+__global__ void rowtab_kernel(RowtabArgs a) {
   const int32_t j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (a.desc) {
+    a.kv_len = a.desc->kv_len;
+    a.patch_tokens = a.desc->patch_tokens;
+    a.n_pos = a.desc->n_tiles * 64;
+  }
   if (j >= a.n_pos) return;
   a.rowtab[j] = row_code(a, j < a.kv_len ? j : 0);
 }
