@@ -372,19 +372,20 @@ def measure_graph(cfg, dev, steps, n_sets=N_INPUT_SETS):
     init = [workloads.gen_step_qkv(cfg, b, 0, cfg.initial_frames, dev) for b in range(B)]
     sets = [[workloads.gen_step_qkv(cfg, b, 1 + i, 1, dev) for b in range(B)] for i in range(n_sets)]
     outs = [torch.empty((T, H, D), dtype=cache.dtype, device=dev) for _ in range(B)]
+    out_init = torch.empty((cfg.initial_frames * T, H, D), dtype=cache.dtype, device=dev)
 
-    def calls(inputs, nq):
+    def calls(inputs, nq, out_bufs):
         for b in range(B):
             q, k, v = inputs[b]
             cache.append_frame(b, k, v)
             if b == 0:
                 cache.evict_frames()
                 cache.plan(nq)
-            cache.run(b, q, outs[b])
+            cache.run(b, q, out_bufs[b])
 
-    calls(init, cfg.initial_frames * T)
+    calls(init, cfg.initial_frames * T, [out_init] * B)
     for f in range(cfg.scale_frames + cfg.sliding_window - cfg.initial_frames):
-        calls(sets[f % n_sets], T)
+        calls(sets[f % n_sets], T, outs)
     graphs = [cache.capture_step(1, [x[1] for x in st], [x[2] for x in st], [x[0] for x in st],
                                  outs) for st in sets]
     torch.cuda.synchronize()
@@ -401,7 +402,7 @@ def measure_graph(cfg, dev, steps, n_sets=N_INPUT_SETS):
         host_graph.append(time.perf_counter() - t1)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        calls(sets[i % n_sets], T)
+        calls(sets[i % n_sets], T, outs)
         host_calls.append(time.perf_counter() - t1)
     torch.cuda.synchronize()
     ns = graphs[0].num_splits()
