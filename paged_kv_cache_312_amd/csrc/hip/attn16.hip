@@ -18,13 +18,14 @@
 //    range (split); each wavefront owns 32 rows;
 //  * 64-key tiles of K and V go from HBM straight into LDS (row-major, global
 //    loads with an LDS destination, no staging registers) through rings of
-//    four stages each, two to three tiles ahead of use; one barrier per tile;
+//    four stages each, one to two tiles ahead of use; one barrier per tile;
 //  * the row codes that address those loads travel the same way, a ring of
 //    eight tiles' codes in LDS, one stage further ahead, so that waiting for
 //    a code never waits for a newer tile;
-//  * software pipeline: each step first issues every LDS operand read it
-//    needs (tile t+1's K, tile t's V), then interleaves tile t+1's K Q^T
-//    MFMAs with tile t's exponentials, then runs tile t's P V MFMAs;
+//  * software pipeline: tile t+1's K Q^T MFMAs start on K operands read during
+//    the previous step and are interleaved with tile t's exponentials; tile
+//    t+2's K operands are read as soon as they are issued; then tile t's P V
+//    MFMAs;
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_{bf16,f16}: a lane then holds 16 scores of
 //    one query row, so the row max needs one exchange with lane +-32 and the
 //    row sum none until the end;
@@ -39,7 +40,12 @@
 //  * with several splits, each writes (O, m, l) partials that a separate merge
 //    kernel combines (a kernel boundary orders them: no fences, which on this
 //    chip would write back and invalidate the XCD's L2 that the workgroups
-//    share).
+//    share);
+//  * one launch may cover several independent streams (a table of per-stream
+//    arguments; each workgroup finds its stream), a skip-append step's own
+//    rows (the TR instances read them from the caller's buffers), and a
+//    graph-replayed step (lengths and tile counts from a step descriptor in
+//    the workspace).
 #include "attn_common.h"
 
 namespace lbm {
