@@ -72,12 +72,18 @@ KERNEL_SOURCES = ["paged_kv_cache_312_amd/csrc/hip/attn16.hip",
 COPY_BYTES = 1 << 30
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(root: str = ROOT) -> str:
+    """Hash of the attention and merge sources with comments and blank space
+    removed (a comment edit does not change the kernel)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(root, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(" ".join(l.split()) for l in text.splitlines() if l.strip()).encode())
     return h.hexdigest()[:16]
 
 
