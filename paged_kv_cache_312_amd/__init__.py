@@ -9,6 +9,7 @@ step of the path runs in the library's HIP kernels and host code.
 from __future__ import annotations
 
 import ctypes
+import weakref
 from ctypes import byref, c_int32, c_int64, c_size_t, c_void_p
 from typing import List, Optional, Sequence, Tuple
 
@@ -235,6 +236,9 @@ class PagedKVCache:
         self.handle = lbm_cache_create(cfg, pps, sps, self.workspace.data_ptr())
 
     def close(self):
+        # graphs captured over this cache go first (they hold its handle)
+        for g in list(getattr(self, "_graphs", ())):
+            g.close()
         if getattr(self, "handle", None):
             lbm_cache_destroy(self.handle)
             self.handle = None
@@ -434,11 +438,16 @@ class StepGraph:
         self.handle = lbm_graph_create(cache.handle, num_frames, [t.data_ptr() for t in ks],
                                        [t.data_ptr() for t in vs], [t.data_ptr() for t in qs],
                                        [t.data_ptr() for t in outs])
+        if not hasattr(cache, "_graphs"):
+            cache._graphs = weakref.WeakSet()
+        cache._graphs.add(self)
 
     def num_splits(self) -> int:
         return lbm_graph_num_splits(self.handle)
 
     def launch(self, stream=None) -> None:
+        if not self.handle:
+            raise ValueError("the graph is closed")
         lbm_graph_launch(self.handle, self.cache._stream(stream))
 
     def close(self) -> None:
