@@ -304,13 +304,14 @@ int32_t choose_splits(int32_t num_q_tokens, int32_t kv_len, int32_t num_heads, i
   };
   if (forced > 0) return normalise(std::min(forced, cap));
   // Cost model, in tile-times of one workgroup alone on a CU, fitted to the
-  // bf16 kernel on MI355X: k workgroups sharing a CU each take
-  // 1 + 0.58 (k - 1) per tile; every workgroup pays a fixed start/finish cost
-  // of about 12 tiles; splitting adds a merge pass (a launch, ~13 tiles, plus
-  // ~1.8 tiles per split of partials).  Equal workgroups are dispatched in
-  // rounds of num_cu * wg_per_cu; the last, partial round spreads its
-  // workgroups over the CUs.
-  constexpr double kShare = 0.58, kFixed = 12.0, kMergeLaunch = 13.0, kMergePerSplit = 1.8;
+  // 16-bit kernel (256 query rows per workgroup) on MI355X: k workgroups
+  // sharing a CU each take 1 + 0.85 (k - 1) per tile (a second workgroup
+  // mostly hides latency; the CU's throughput grows little); every workgroup
+  // pays a start/finish cost of about 2 tiles; splitting adds a merge pass (a
+  // launch, ~13 tiles, plus ~4 tiles per split of partials).  Equal
+  // workgroups are dispatched in rounds of num_cu * wg_per_cu; the last,
+  // partial round spreads its workgroups over the CUs.
+  constexpr double kShare = 0.85, kFixed = 2.0, kMergeLaunch = 13.0, kMergePerSplit = 4.0;
   const int64_t units = int64_t(ceil_div(num_q_tokens, kRowsPerGroup)) * num_heads;
   const int64_t slots = int64_t(num_cu) * wg_per_cu;
   auto per_tile = [&](int64_t k) { return 1.0 + kShare * double(k - 1); };

@@ -30,7 +30,8 @@ namespace lbm {
 
 constexpr int32_t kMaxStepFrames = 128;        // frames one append may bring
 constexpr int32_t kMaxStepSpecialPages = 256;  // special pages one append may touch
-constexpr int32_t kRowsPerGroup = 128;         // query rows per attention workgroup
+constexpr int32_t kRowsPerGroup = 256;         // query rows per 16-bit attention workgroup (and
+                                               // the padding of partial-result rows)
 constexpr int32_t kKeysPerTile = 64;           // keys per attention tile
 constexpr int32_t kSplitMax = 16;              // most key-range splits of one run
 constexpr int32_t kSplitRowCap = 2048;         // partial-result rows budgeted per split

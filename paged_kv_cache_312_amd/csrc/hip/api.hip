@@ -29,12 +29,12 @@ int32_t attn_occupancy(int32_t dtype, int32_t head_dim) {
   return dtype == LBM_F32 ? attn_occupancy_f32(head_dim) : attn_occupancy16();
 }
 
-void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits) {
+void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits, int32_t rows_per_wg) {
   a->n_tiles = (a->kv_len + kKeysPerTile - 1) / kKeysPerTile;
   a->tiles_per_split = (a->n_tiles + num_splits - 1) / num_splits;
   a->num_splits = (a->n_tiles + a->tiles_per_split - 1) / a->tiles_per_split;
-  a->n_qt = (a->Tq + kRowsPerGroup - 1) / kRowsPerGroup;
-  a->rows_pad = a->n_qt * kRowsPerGroup;
+  a->n_qt = (a->Tq + rows_per_wg - 1) / rows_per_wg;
+  a->rows_pad = (a->Tq + kRowsPerGroup - 1) / kRowsPerGroup * kRowsPerGroup;
   a->total_items = a->n_qt * a->H * a->num_splits;
   a->items_per_xcd = (a->total_items + 7) / 8;
   a->scale_log2 = float(1.4426950408889634 / std::sqrt(double(head_dim)));
@@ -176,7 +176,8 @@ lbm_status launch_attention_batch(const lbm_config& c, AttnArgs* as, int32_t n, 
   std::memset(&b, 0, sizeof(b));
   b.n = n;
   for (int32_t i = 0; i < n; ++i) {
-    finish_attn_args(&as[i], c.head_dim, splits);
+    finish_attn_args(&as[i], c.head_dim, splits,
+                     c.dtype == LBM_F32 ? kRowsPerWGf32 : kRowsPerWG16);
     b.s[i] = as[i];
     b.item_start[i + 1] = b.item_start[i] + as[i].total_items;
   }

@@ -14,29 +14,33 @@
 // and the conversions.
 //
 // Structure (D = 64):
-//  * a workgroup = 4 wavefronts = 128 query rows of one head over one key
-//    range (split); each wavefront owns 32 rows;
+//  * a workgroup = 4 wavefronts = 256 query rows of one head over one key
+//    range (split); each wavefront owns 64 rows as two halves of 32, so every
+//    K and V operand read from LDS feeds two MFMAs.  A wavefront whose rows
+//    all lie past the step's queries only loads its share of each tile and
+//    keeps the barriers, so the step's last query group proceeds in step with
+//    the groups that share its key range (and its tiles in L2);
 //  * 64-key tiles of K and V go from HBM straight into LDS (row-major, global
 //    loads with an LDS destination, no staging registers) through rings of
-//    four stages each, one to two tiles ahead of use; one barrier per tile;
+//    four stages each, three tiles ahead of use; one barrier per tile;
 //  * the row codes that address those loads travel the same way, a ring of
-//    eight tiles' codes in LDS, one stage further ahead, so that waiting for
+//    eight tiles' codes in LDS, three tiles further ahead, so that waiting for
 //    a code never waits for a newer tile;
-//  * software pipeline: tile t+1's K Q^T MFMAs start on K operands read during
-//    the previous step and are interleaved with tile t's exponentials; tile
-//    t+2's K operands are read as soon as they are issued; then tile t's P V
-//    MFMAs;
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_{bf16,f16}: a lane then holds 16 scores of
-//    one query row, so the row max needs one exchange with lane +-32 and the
-//    row sum none until the end;
+//    one query row per half, so the row max needs one exchange with lane +-32
+//    and the row sum none until the end;
 //  * per-step row table (one code per key position) gives each K/V row's
 //    address, so the loop does no page arithmetic;
-//  * online softmax in fp32 with exp2 and the scale folded in, against a
-//    running max that is refreshed (and O rescaled) only when a weight would
-//    exceed 256; row sums by 16-bit dot products of the rounded weights;
+//  * online softmax in fp32 with exp2 and the scale folded into Q, against a
+//    running max that the score MFMAs subtract themselves (their accumulators
+//    start from -max) and that is refreshed (O rescaled, the tile's scores
+//    recomputed from LDS) only when a weight would exceed 256; row sums by
+//    16-bit dot products of the rounded weights;
 //  * O^T += V^T P^T on the same MFMA with P taken from registers (no LDS trip),
 //    P rounded to the input type (round to nearest even); the V operand comes from the
 //    row-major tile through gfx950's LDS transpose reads;
+//  * 226 VGPRs and no scratch, two workgroups per CU: a second workgroup
+//    on each SIMD overlaps one wavefront's exponentials with the other's MFMAs;
 //  * with several splits, each writes (O, m, l) partials that a separate merge
 //    kernel combines (a kernel boundary orders them: no fences, which on this
 //    chip would write back and invalidate the XCD's L2 that the workgroups
@@ -85,9 +89,15 @@ constexpr int LS = 64;              // LDS row = one key's 64 columns, 128 bytes
 constexpr int TILE = 64 * LS;       // elements of one staged K or V tile
 constexpr int NST = 4;              // LDS stages of K and of V
 constexpr int NCODE = 2 * NST;      // LDS slots of row codes (64 per tile)
+constexpr int kLead = NST - 1;      // tiles whose K and V are loaded ahead of use
 // Global loads (all with an LDS destination) each wavefront issues per tile:
-// two K, two V, one of row codes.
-constexpr int kLoadsPerStep = 5;
+// two K, two V, then one of row codes.
+constexpr int kLoadsKV = 4;
+constexpr int kLoadsPerStep = kLoadsKV + 1;
+// Loads a wavefront may leave outstanding at the end of a step: this step's
+// and, in the first step, the prologue's loads of position kLead-1.
+constexpr int kInFlight = kLoadsPerStep + kLoadsKV;
+static_assert(NCODE > 2 * kLead, "a code slot is reloaded only after its read");
 
 // s_waitcnt with only the vector-memory count constrained (expcnt and
 // lgkmcnt at their maxima); n < 64.
@@ -162,6 +172,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     a.tiles_per_split = a.desc->tiles_per_split;
     a.tr_start = a.kv_len;
   }
+  // item -> (query group, head, key range); the groups sharing a key range
+  // are consecutive items, so they run side by side on one L2
   const int32_t qt = item % a.n_qt;
   const int32_t grp = item / a.n_qt;
   const int32_t head = grp / a.num_splits;
@@ -173,41 +185,55 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   const int32_t HD = a.H * D;
   const int32_t t_begin = split * a.tiles_per_split;
   const int32_t t_end = min(a.n_tiles, t_begin + a.tiles_per_split);
+  // Rows: wavefront w owns rows 64w .. 64w+63 of the group's 256, as two
+  // halves of 32; this lane's row in half h is qrow0 + 32h.
+  const int32_t w_row0 = qt * kRowsPerWG16 + wave * 64;
+  const int32_t qrow0 = w_row0 + l32;
   if (t_end <= t_begin) {
     // a split left without keys (graph-replayed steps keep the capture's split
     // count): an empty partial, weight 0 in the merge
-    const int32_t qrow0 = qt * 128 + wave * 32 + l32;
-    if (qrow0 < a.Tq) {
-      const size_t rh = (size_t(split) * a.rows_pad + qrow0) * a.H + head;
-      float* po = a.part_o + rh * D;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+    for (int h = 0; h < 2; ++h) {
+      const int32_t qrow = qrow0 + 32 * h;
+      if (qrow < a.Tq) {
+        const size_t rh = (size_t(split) * a.rows_pad + qrow) * a.H + head;
+        float* po = a.part_o + rh * D;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<float4*>(po + db * 32 + 8 * i + 4 * hh) = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + rh * 2) = make_float2(-INFINITY, 0.f);
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<float4*>(po + db * 32 + 8 * i + 4 * hh) = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + rh * 2) = make_float2(-INFINITY, 0.f);
+      }
     }
     return;
   }
+  // a wavefront whose rows are all past the step's queries only loads its
+  // share of every tile and keeps the workgroup's barriers (the last query
+  // group's wavefronts beyond its rows)
+  const bool idle = w_row0 >= a.Tq;
 
-  // Q as the B operand of S^T = K Q^T: row `qrow`, columns 16ks + 8hh .. +7,
-  // pre-multiplied by log2(e)/sqrt(D) (rounded to T) so that the MFMA
+  // Q as the B operand of S^T = K Q^T: half h's row, columns 16ks + 8hh ..
+  // +7, pre-multiplied by log2(e)/sqrt(D) (rounded to T) so that the MFMA
   // yields scores in base-2 exponent units.
   const float c = a.scale_log2;
-  const int32_t qrow = qt * 128 + wave * 32 + l32;
-  h8 qf[4];
-  if (qrow < a.Tq) {
-    const h8* qp = reinterpret_cast<const h8*>(
-        reinterpret_cast<const uint16_t*>(a.q) + size_t(qrow) * HD + head * D + 8 * hh);
+  h8 qf[2][4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const h8 x = qp[2 * ks];
+  for (int h = 0; h < 2; ++h) {
+    const int32_t qrow = qrow0 + 32 * h;
+    if (qrow < a.Tq) {
+      const h8* qp = reinterpret_cast<const h8*>(
+          reinterpret_cast<const uint16_t*>(a.q) + size_t(qrow) * HD + head * D + 8 * hh);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) qf[ks][u] = static_cast<T>(static_cast<float>(x[u]) * c);
+      for (int ks = 0; ks < 4; ++ks) {
+        const h8 x = qp[2 * ks];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) qf[h][ks][u] = static_cast<T>(static_cast<float>(x[u]) * c);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qf[h][ks] = h8{};
     }
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = h8{};
   }
 
   // Loads into LDS: a wavefront instruction fills 1 KB = 8 rows of 128 B,
@@ -231,33 +257,36 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     const int32_t off = v ? v_col + (special ? a.vstride_special : a.vstride_patch) : k_col;
     return base + (code & 0x7fffffffu) + off;
   };
-  // Skip-append step: keys in [tr_start, kv_len) of tile position x come from
-  // the frame's own rows (the row table holds position 0's code there, like
-  // the padding past kv_len, which keeps its code).  The test is uniform per
-  // tile, so tiles of cached keys take the plain path.
-  auto own_rows = [&](int32_t x, bool v, const char*& p0, const char*& p1)
-                      __attribute__((always_inline)) {
+  // K and V of tile position x into stage x mod NST.  Skip-append step: keys
+  // in [tr_start, kv_len) come from the frame's own rows (the row table holds
+  // position 0's code there, like the padding past kv_len, which keeps its
+  // code); the test is uniform per tile, and only the step's last tiles take
+  // that branch.
+  auto load_kv = [&](int32_t x, uint2 c) __attribute__((always_inline)) {
+    const int32_t stage = x & (NST - 1);
+    const char* k0 = row_ptr(c.x, false);
+    const char* k1 = row_ptr(c.y, false);
+    const char* v0 = row_ptr(c.x, true);
+    const char* v1 = row_ptr(c.y, true);
     const int32_t t0 = tile_at(x) * 64;
-    if (t0 + 64 > a.tr_start) {
-      const char* base = static_cast<const char*>(v ? a.tv : a.tk) + (v ? v_col : k_col);
-      const int32_t k0 = t0 + lp, k1 = t0 + lp + 32;
-      if (k0 >= a.tr_start && k0 < a.kv_len) p0 = base + size_t(k0 - a.tr_start) * a.row_bytes;
-      if (k1 >= a.tr_start && k1 < a.kv_len) p1 = base + size_t(k1 - a.tr_start) * a.row_bytes;
+    if (TR && t0 + 64 > a.tr_start) {
+      const char* tk = static_cast<const char*>(a.tk) + k_col;
+      const char* tv = static_cast<const char*>(a.tv) + v_col;
+      const int32_t j0 = t0 + lp - a.tr_start, j1 = j0 + 32;
+      const int32_t n_own = a.kv_len - a.tr_start;
+      if (j0 >= 0 && j0 < n_own) {
+        k0 = tk + size_t(j0) * a.row_bytes;
+        v0 = tv + size_t(j0) * a.row_bytes;
+      }
+      if (j1 >= 0 && j1 < n_own) {
+        k1 = tk + size_t(j1) * a.row_bytes;
+        v1 = tv + size_t(j1) * a.row_bytes;
+      }
     }
-  };
-  auto load_k = [&](int32_t stage, uint2 c, int32_t x) __attribute__((always_inline)) {
-    const char* p0 = row_ptr(c.x, false);
-    const char* p1 = row_ptr(c.y, false);
-    if (TR) own_rows(x, false, p0, p1);
-    load_to_lds<16>(p0, &lds_k[stage][(8 * wave) * LS]);
-    load_to_lds<16>(p1, &lds_k[stage][(32 + 8 * wave) * LS]);
-  };
-  auto load_v = [&](int32_t stage, uint2 c, int32_t x) __attribute__((always_inline)) {
-    const char* p0 = row_ptr(c.x, true);
-    const char* p1 = row_ptr(c.y, true);
-    if (TR) own_rows(x, true, p0, p1);
-    load_to_lds<16>(p0, &lds_v[stage][(8 * wave) * LS]);
-    load_to_lds<16>(p1, &lds_v[stage][(32 + 8 * wave) * LS]);
+    load_to_lds<16>(k0, &lds_k[stage][(8 * wave) * LS]);
+    load_to_lds<16>(k1, &lds_k[stage][(32 + 8 * wave) * LS]);
+    load_to_lds<16>(v0, &lds_v[stage][(8 * wave) * LS]);
+    load_to_lds<16>(v1, &lds_v[stage][(32 + 8 * wave) * LS]);
   };
   // all 64 codes of tile position x into their slot (every wavefront loads
   // the whole slice, so each one waits only for its own loads)
@@ -277,6 +306,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
+  // Step i's loads: K and V of position i+kLead (into the stage read in step
+  // i-1, with the codes read at the end of step i-1) and the codes of
+  // position i+2kLead.  At the end of step i the wavefront waits until at
+  // most kInFlight of its loads are outstanding: position i+1's K and V and
+  // position i+kLead+1's codes have then landed (issued in step i+1-kLead or,
+  // for the first steps, in the prologue); those codes are read before the
+  // barrier, so their LDS latency overlaps it.
+  uint2 code_nx;  // codes of the position the next step loads
+  auto step_loads = [&](int32_t i) __attribute__((always_inline)) {
+    load_kv(i + kLead, code_nx);
+    load_codes(i + 2 * kLead);
+  };
+  auto end_step = [&](int32_t i) __attribute__((always_inline)) {
+    LBM_WAIT_VMCNT_LDS0(kInFlight);
+    code_nx = codes_of(i + 1 + kLead);
+    barrier();
+  };
 
   // K operand: row kb*32 + l32, chunk 2ks + hh (swizzle depends on l32 only).
   // V transpose read: within each 16-lane group g, lane s points at row
@@ -292,54 +338,62 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   const int v_rd0 = v_row + (((0 * 4 + v_c) ^ v_x) * 8) + 4 * (s16 & 1);
   const int v_rd1 = v_row + (((1 * 4 + v_c) ^ v_x) * 8) + 4 * (s16 & 1);
 
-  // the 8 K operands of a tile (S^T = K Q^T, key blocks kb, column steps ks)
-  auto k_reads = [&](const uint16_t* K, h8* kf) __attribute__((always_inline)) {
+  f32x16 o[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        kf[kb * 4 + ks] = *reinterpret_cast<const h8*>(
-            K + k_row + kb * 32 * LS + (((2 * ks + hh) ^ k_x) * 8));
-  };
-  // the 8 V operands of a tile (O^T = V^T P^T, column blocks db, key groups G)
-  auto v_reads = [&](const uint16_t* V, h8* vf) __attribute__((always_inline)) {
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int G = 0; G < 4; ++G) {
-        const uint16_t* p = V + (db == 0 ? v_rd0 : v_rd1) + (16 * G) * LS;
-        vf[db * 4 + G] = v_operand<h8>(p, p + 8 * LS);
-      }
-  };
-  // S^T[key][row] - m of one tile, in base-2 units: lane holds row l32 and
-  // keys kb*32 + 8i + 4hh + j; the accumulator starts from `neg_m` (every
-  // element -m), so the running max is subtracted by the MFMA itself.
-  auto qk = [&](const h8* kf, f32x16* s, const f32x16& neg_m) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = Elt<T>::mfma(kf[kb * 4], qf[0], neg_m);
-#pragma unroll
-      for (int ks = 1; ks < 4; ++ks)
-        s[kb] = Elt<T>::mfma(kf[kb * 4 + ks], qf[ks], s[kb]);
-    }
-  };
-
-  f32x16 o[2];
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
-  float m_run = 0.f;  // running max of this row's scores in base-2 units (stale between jumps)
-  float l_run = 0.f;  // this lane's share of the row sum, relative to m_run
-  f32x16 neg_m;       // -m_run in every element: the QK accumulator start
-#pragma unroll
-  for (int e = 0; e < 16; ++e) neg_m[e] = 0.f;
+      for (int e = 0; e < 16; ++e) o[h][db][e] = 0.f;
+  // per half: running max of the row's scores in base-2 units (stale between
+  // jumps) and this lane's share of the row sum relative to it
+  float m_run[2] = {0.f, 0.f};
+  float l_run[2] = {0.f, 0.f};
   const h2 ones = {static_cast<T>(1.0f), static_cast<T>(1.0f)};
 
-  // p = 2^(s - shift) in T (s already relative to m_run), grouped as the
-  // B operand of the PV MFMA (group G = 2kb + g holds elements 8g..8g+7 of
-  // s[kb]); returns this lane's sum of the rounded p (exactly the weights the
-  // PV product uses).  shift is 0 except after a refresh of the max.
+  // S^T[key][row] - m of tile position i for both halves, in base-2 units:
+  // lane holds row l32 (+32h) and keys kb*32 + 8j + 4hh + u (element 4j + u
+  // of s[h][kb]); each K operand read feeds both halves' MFMAs.  Each
+  // accumulator starts from -m_run in every element, so the MFMAs subtract
+  // the running max themselves; the start is written into the accumulator's
+  // own registers each tile (the asm keeps the compiler from carrying a
+  // broadcast copy of -m across the loop, which would cost 16 registers per
+  // half).  On the split's last tile, keys past the visible set are masked.
+  auto scores = [&](int32_t i, bool last, f32x16 (*s)[2]) __attribute__((always_inline)) {
+    const uint16_t* K = lds_k[i & (NST - 1)];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float nm = -m_run[h];
+      asm volatile("" : "+v"(nm));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[h][kb][e] = nm;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const h8 kf = *reinterpret_cast<const h8*>(K + k_row + kb * 32 * LS +
+                                                   (((2 * ks + hh) ^ k_x) * 8));
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          s[h][kb] = Elt<T>::mfma(kf, qf[h][ks], s[h][kb]);
+      }
+    if (last) {
+      const int32_t lim = a.kv_len - (t_begin + i) * 64 - 4 * hh;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            s[h][kb][e] = kb * 32 + 8 * (e >> 2) + (e & 3) >= lim ? -INFINITY : s[h][kb][e];
+    }
+  };
+  // p = 2^(s - shift) in T, grouped as the B operand of the PV MFMA (group
+  // G = 2kb + g holds elements 8g..8g+7 of s[kb]); returns this lane's sum of
+  // the rounded p (exactly the weights the PV product uses).
   auto exponentiate = [&](const f32x16* s, float shift, h8* pb) __attribute__((always_inline)) {
     float lt[2] = {0.f, 0.f};
 #pragma unroll
@@ -358,159 +412,117 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
       }
     return lt[0] + lt[1];
   };
+  // the row's tile max minus m_run (both lanes of the row agree)
+  auto row_max = [&](const f32x16* s) __attribute__((always_inline)) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+    return fmaxf(mx, __shfl_xor(mx, 32));
+  };
 
-  // Prologue: row codes of tile positions 0 .. 2NST-1; K of positions
-  // 0 .. NST-1 and V of 0 .. NST-2; then S of position 0.  Step i (below)
-  // loads the codes of position i+2NST, reads those of i+NST and loads K of
-  // i+NST with them, and V of i+NST-1 with the codes read one step earlier.
+  // One tile: scores, weights, and O += P V for both halves.  Softmax runs
+  // against the running max as it stands (the scores arrive with it
+  // subtracted).  On the split's first tile the max is the tile's own, so the
+  // largest weight is 1 and the row sum never underflows; afterwards the max
+  // is raised only when some lane's weights would sum past 256 (a jump of
+  // the max), and then that tile's scores are recomputed from the stage
+  // (still resident until the step's barrier), O and l rescaled and the
+  // weights redone.  Any max not below the true one gives the same quotient,
+  // since numerator and denominator share it.
+  auto tile = [&](int32_t i, bool first, bool last) __attribute__((always_inline)) {
+    f32x16 s[2][2];
+    h8 pb[2][4];
+    float lt[2] = {0.f, 0.f};
+    scores(i, last, s);
+    if (first) {
 #pragma unroll
-  for (int x = 0; x < NCODE; ++x) load_codes(x);
-  LBM_WAIT_VMCNT(0);
-  asm volatile("" ::: "memory");  // the code reads below stay after the wait
-  uint2 code_v;
+      for (int h = 0; h < 2; ++h) {
+        const float mx = row_max(s[h]);
+        m_run[h] = mx;
+        lt[h] = exponentiate(s[h], mx, pb[h]);
+      }
+    } else {
 #pragma unroll
-  for (int x = 0; x < NST; ++x) {
-    code_v = codes_of(x);
-    load_k(x, code_v, x);
-    if (x < NST - 1) load_v(x, code_v, x);
-  }
-  // code_v: position NST-1, for the V load of step 0
-  LBM_WAIT_VMCNT_LDS0(0);
-  barrier();
-  f32x16 s_a[2], s_b[2];
-  h8 kf[8];  // K operands of the next tile position's K Q^T
-  k_reads(lds_k[0], kf);
-  qk(kf, s_a, neg_m);
-  k_reads(lds_k[1], kf);
-  LBM_WAIT_VMCNT_LDS0(63);  // stage 0 of K is reloaded in the first step
-  barrier();
-
-  // Softmax against the running max as it stands (the scores arrive with it
-  // subtracted); the row max of the tile is taken on the split's first tile
-  // and whenever some weight would leave [0, 256] (a jump of the max): then O
-  // and l are rescaled and the tile redone.  Any max that is not below the
-  // true one gives the same quotient, since numerator and denominator share
-  // it; the first tile's refresh makes the largest weight 1, so the row sum
-  // never underflows.
-  // s_nxt (nullable): the next tile's scores, already issued relative to the
-  // old max, are moved to the new one.
-  auto refresh_max = [&](const f32x16* s_cur, f32x16* s_nxt, h8* pb, float& lt, bool first)
-                         __attribute__((always_inline)) {
-    if (__ballot(!(lt <= 256.f)) || first) {
-      float mx = s_cur[0][0];
+      for (int h = 0; h < 2; ++h) lt[h] = exponentiate(s[h], 0.f, pb[h]);
+      if (__ballot(!(lt[0] <= 256.f) || !(lt[1] <= 256.f))) {
+        scores(i, last, s);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int h = 0; h < 2; ++h) {
+          const float step_up = fmaxf(row_max(s[h]), 0.f);
+          const float alpha = fast_exp2(-step_up);
+          l_run[h] *= alpha;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s_cur[kb][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));  // tile max - m_run
-      const float step_up = first ? mx : fmaxf(mx, 0.f);
-      const float alpha = first ? 0.f : fast_exp2(-step_up);
-      l_run *= alpha;
+          for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-      lt = exponentiate(s_cur, step_up, pb);
-      m_run += step_up;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) neg_m[e] = -m_run;
-      if (s_nxt) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) s_nxt[kb][e] -= step_up;
+            for (int e = 0; e < 16; ++e) o[h][db][e] *= alpha;
+          lt[h] = exponentiate(s[h], step_up, pb[h]);
+          m_run[h] += step_up;
+        }
       }
     }
-  };
-  // O^T[d][row] += V^T[d][keys] P^T[keys][row]
-  auto pv = [&](const h8* vf, const h8* pb) __attribute__((always_inline)) {
+    l_run[0] += lt[0];
+    l_run[1] += lt[1];
+    // O^T[d][row] += V^T[d][keys] P^T[keys][row]; each V operand read feeds
+    // both halves' MFMAs
+    const uint16_t* V = lds_v[i & (NST - 1)];
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int G = 0; G < 4; ++G)
-        o[db] = Elt<T>::mfma(vf[db * 4 + G], pb[G], o[db]);
+      for (int G = 0; G < 4; ++G) {
+        const uint16_t* p = V + (db == 0 ? v_rd0 : v_rd1) + (16 * G) * LS;
+        const h8 vf = v_operand<h8>(p, p + 8 * LS);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) o[h][db] = Elt<T>::mfma(vf, pb[h][G], o[h][db]);
+      }
   };
 
-  // Steady-state step for tile position i (not the split's last): s_cur
-  // holds its scores, s_nxt receives position i+1's, whose K operands are
-  // already in registers (read during step i-1), so its K Q^T MFMAs start at
-  // once and are interleaved with position i's exponentials: the matrix
-  // cores run while the vector ALUs work.  The step's loads into LDS (to
-  // stages last read in the previous step) and its V operand reads go out
-  // first; position i+2's K operands are read once the K Q^T MFMAs have
-  // consumed i+1's.  At the end each wavefront waits for its loads of step
-  // i-1 (position i+3's K, the next step's V and codes), then the barrier
-  // publishes them to the workgroup.
-  auto step = [&](int32_t i, f32x16* s_cur, f32x16* s_nxt) __attribute__((always_inline)) {
-    const uint2 code_k = codes_of(i + NST);
-    load_codes(i + 2 * NST);
-    h8 vf[8], pb[4];
-    v_reads(lds_v[i & (NST - 1)], vf);
-    load_k(i & (NST - 1), code_k, i + NST);
-    load_v((i + NST - 1) & (NST - 1), code_v, i + NST - 1);
-    qk(kf, s_nxt, neg_m);
-    float lt = exponentiate(s_cur, 0.f, pb);
-    k_reads(lds_k[(i + 2) & (NST - 1)], kf);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // codes
-    __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // first exponentials
+  // Prologue: row codes of positions 0 .. 2kLead-1, then K and V of
+  // positions 0 .. kLead-1; position 0 resident before the first step.
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      if (u == 1) __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // V reads
-      if (u == 7) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // next K reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // ten VALU
+  for (int x = 0; x < 2 * kLead; ++x) load_codes(x);
+  LBM_WAIT_VMCNT(0);
+  asm volatile("" ::: "memory");  // the code reads below stay after the wait
+#pragma unroll
+  for (int x = 0; x < kLead; ++x) load_kv(x, codes_of(x));
+  LBM_WAIT_VMCNT_LDS0(kLoadsKV * (kLead - 1));
+  barrier();
+  code_nx = codes_of(kLead);
+
+  // The same barriers on every wavefront: one after the prologue and one
+  // after each step but the last.
+  if (idle) {
+    for (int32_t i = 0; i + 1 < n_t; ++i) {
+      step_loads(i);
+      end_step(i);
     }
-    refresh_max(s_cur, s_nxt, pb, lt, i == 0);
-    l_run += lt;
-    pv(vf, pb);
-    code_v = code_k;
-    // this wavefront's reads of the stages refilled next step are complete
-    // (the compiler may sink their consumers past the barrier), and its
-    // loads of step i-1 have landed
-    LBM_WAIT_VMCNT_LDS0(kLoadsPerStep * (NST - 3));
-    barrier();
-  };
-  // The split's last tile: no next tile; keys past the visible set masked.
-  auto last_step = [&](int32_t i, f32x16* s_cur) __attribute__((always_inline)) {
-    const int32_t t = t_begin + i;
-    {
-      // element e of s_cur[kb] is key t*64 + 4hh + (kb*32 + 8(e/4) + e%4);
-      // applied unconditionally (once per split) to keep one copy of s_cur
-      const int32_t lim = a.kv_len - t * 64 - 4 * hh;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          s_cur[kb][e] = kb * 32 + 8 * (e >> 2) + (e & 3) >= lim ? -INFINITY : s_cur[kb][e];
+    LBM_WAIT_VMCNT(0);
+    return;
+  }
+  if (n_t == 1) {
+    tile(0, true, true);
+  } else {
+    step_loads(0);
+    tile(0, true, false);
+    end_step(0);
+    for (int32_t i = 1; i + 1 < n_t; ++i) {
+      step_loads(i);
+      tile(i, false, false);
+      end_step(i);
     }
-    h8 vf[8], pb[4];
-    v_reads(lds_v[i & (NST - 1)], vf);
-    float lt = exponentiate(s_cur, 0.f, pb);
-    refresh_max(s_cur, nullptr, pb, lt, i == 0);
-    l_run += lt;
-    pv(vf, pb);
-  };
-  // unrolled by two so that the two score buffers swap roles instead of
-  // being copied
-  int32_t i = 0;
-  for (; i + 2 < n_t; i += 2) {
-    step(i, s_a, s_b);
-    step(i + 1, s_b, s_a);
+    tile(n_t - 1, false, true);
   }
-  if (n_t - i == 2) {
-    step(i, s_a, s_b);
-    s_a[0] = s_b[0];  // one inlined copy of the last step
-    s_a[1] = s_b[1];
-    ++i;
-  }
-  last_step(i, s_a);
 
   // loads of clamped positions may still be in flight: the workgroup's LDS
   // must not be released under them
   LBM_WAIT_VMCNT(0);
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (a.num_splits == 1) {
-    if (qrow < a.Tq) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int32_t qrow = qrow0 + 32 * h;
+    if (qrow >= a.Tq) continue;
+    const float l_tot = l_run[h] + __shfl_xor(l_run[h], 32);
+    if (a.num_splits == 1) {
       const float inv = 1.f / l_tot;
       T* op = reinterpret_cast<T*>(a.out) + size_t(qrow) * HD + head * D;
 #pragma unroll
@@ -520,23 +532,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
           typedef T h4 __attribute__((ext_vector_type(4)));
           h4 w;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) w[j] = static_cast<T>(o[db][4 * i + j] * inv);
+          for (int j = 0; j < 4; ++j) w[j] = static_cast<T>(o[h][db][4 * i + j] * inv);
           *reinterpret_cast<h4*>(op + db * 32 + 8 * i + 4 * hh) = w;
         }
+    } else {
+      const size_t rh = (size_t(split) * a.rows_pad + qrow) * a.H + head;
+      float* po = a.part_o + rh * D;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<float4*>(po + db * 32 + 8 * i + 4 * hh) =
+              make_float4(o[h][db][4 * i], o[h][db][4 * i + 1], o[h][db][4 * i + 2],
+                          o[h][db][4 * i + 3]);
+      if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + rh * 2) = make_float2(m_run[h], l_tot);
     }
-    return;
-  }
-
-  if (qrow < a.Tq) {
-    const size_t rh = (size_t(split) * a.rows_pad + qrow) * a.H + head;
-    float* po = a.part_o + rh * D;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<float4*>(po + db * 32 + 8 * i + 4 * hh) =
-            make_float4(o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]);
-    if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + rh * 2) = make_float2(m_run, l_tot);
   }
 }
 

@@ -18,7 +18,7 @@
 
 namespace lbm {
 
-constexpr int kThreads = 256;  // 4 wavefronts of 64, 32 query rows each
+constexpr int kThreads = 256;  // 4 wavefronts of 64 lanes
 
 // Work item of workgroup `blk`: consecutive items go to one XCD (workgroup i
 // runs on XCD i mod 8), so the query groups sharing one head's key range run

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const BatchArgs b) {
   if (t_end <= t_begin) {
     // a split left without keys (graph-replayed steps keep the capture's split
     // count): an empty partial, weight 0 in the merge
-    const int32_t qrow0 = qt * 128 + wave * 32 + l32;
+    const int32_t qrow0 = qt * kRowsPerWGf32 + wave * 32 + l32;
     if (qrow0 < a.Tq) {
       const size_t rh = (size_t(split) * a.rows_pad + qrow0) * a.H + head;
       float* po = a.part_o + rh * D;
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const BatchArgs b) {
   }
 
   // Q as the B operand: row qrow, contraction columns HALF*hh + ks.
-  const int32_t qrow = qt * 128 + wave * 32 + l32;
+  const int32_t qrow = qt * kRowsPerWGf32 + wave * 32 + l32;
   float qf[HALF];
   if (qrow < a.Tq) {
     const float4* qp = reinterpret_cast<const float4*>(

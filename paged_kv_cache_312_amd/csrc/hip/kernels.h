@@ -73,8 +73,8 @@ struct AttnArgs {
   const StepDesc* desc;
   int32_t n_tiles;            // ceil(kv_len / 64)
   int32_t num_splits, tiles_per_split;
-  int32_t n_qt;               // ceil(Tq / 128)
-  int32_t rows_pad;           // n_qt * 128
+  int32_t n_qt;               // ceil(Tq / rows per workgroup of the kernel)
+  int32_t rows_pad;           // ceil(Tq / kRowsPerGroup) * kRowsPerGroup
   int32_t total_items;        // n_qt * H * num_splits
   int32_t items_per_xcd;      // ceil(total_items / 8)
   float scale_log2;           // log2(e) / sqrt(D)
@@ -92,8 +92,15 @@ struct BatchArgs {
   AttnArgs s[kMaxBatch];
 };
 
-// Fill the split/grid fields of `a` for a launch (Tq, kv_len, splits known).
-void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits);
+// Query rows per workgroup: the 16-bit kernel (4 wavefronts x 64) and the
+// fp32 kernel (4 x 32).
+constexpr int32_t kRowsPerWG16 = kRowsPerGroup;
+constexpr int32_t kRowsPerWGf32 = 128;
+static_assert(kRowsPerGroup % kRowsPerWGf32 == 0, "partial rows cover both kernels' groups");
+
+// Fill the split/grid fields of `a` for a launch (Tq, kv_len, splits known)
+// by a kernel with `rows_per_wg` query rows per workgroup.
+void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits, int32_t rows_per_wg);
 
 // 16-bit inputs: bf16, or fp16 when `fp16`; `transient`: a skip-append step
 // (tr_start < kv_len)

@@ -188,7 +188,7 @@ def test_core_rejects_bad_config(bad):
 
 def test_choose_splits():
     cs = CoreBookkeeping.choose_splits
-    # the 24-block ViT-L step: 11 query groups x 16 heads, ~1.55k tiles
+    # the 24-block ViT-L step: 6 query groups x 16 heads, ~1.55k tiles
     ns = cs(1375, 99006, 16, 256, 2, 16)
     assert 4 <= ns <= 12
     # the 8-frame first step fills the chip without splitting
