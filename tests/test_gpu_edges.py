@@ -1,0 +1,100 @@
+"""Edge cases of the attention kernels through the stateless entry point
+(lbm_paged_attention), where the caller's tables set the visible length
+freely: lengths at and around the 64-key tile edges (one key, a partial
+tile, exact tiles, a patch page plus a ragged special tail), query counts at
+the edges of the kernels' row blocks (32-row halves, 64-row wavefronts,
+128- and 256-row workgroups, the configured maximum), split counts from the
+planner's to more splits than tiles, and every dtype.
+
+Expected values: dense softmax attention (the oracle, fp64) over the visible
+rows gathered in table order -- the listed patch pages, P tokens each, then
+the first n_special_tokens tokens of the listed special pages ("How FlashInfer's
+Paged KV Cache Attention Outperforms SDPA Fallback in Streaming Inference",
+FAQ on variable sequence lengths; "How the Paged KV Cache Attention Mechanism
+Enables Long Sequence Inference in LingBot-Map", "Building the Visible Page
+Table").  Inputs are seeded unit-normal draws shared by both sides."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_312_amd as lbm
+import workloads
+from gpu_helpers import DEV, compare, say
+from oracle import dense_attention
+
+pytestmark = pytest.mark.gpu
+
+P, SPS, H = 100, 16, 2          # patch page tokens, special page tokens, heads
+N_PP, N_SP = 12, 12             # pages in each pool
+MAX_Q = 300
+DTYPE_CODE = {"bf16": 0, "f32": 1, "f16": 2}
+
+# (patch pages, special tokens) -> visible length
+KV_CASES = [(0, 1), (0, 63), (0, 64), (0, 65), (1, 0), (1, 27), (1, 28), (1, 29), (2, 27),
+            (10, 0), (10, 191)]
+TQ_CASES = [1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, MAX_Q]
+SPLITS = [0, 1, 3, 16]
+
+
+def _config(dtype: str, head_dim: int, splits: int):
+    return lbm.make_config(num_blocks=1, num_heads=H, head_dim=head_dim, patches_per_frame=P,
+                           special_per_frame=6, special_page_size=SPS, scale_frames=2,
+                           sliding_window=8, max_patch_pages=N_PP, max_special_pages=N_SP,
+                           max_frames_per_step=1, max_q_tokens=MAX_Q, dtype=DTYPE_CODE[dtype],
+                           num_splits=splits)
+
+
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 64), ("f16", 64), ("f32", 64), ("f32", 32)])
+def test_tile_and_row_edges(dtype, head_dim):
+    D = head_dim
+    seed0 = 9100 + 10 * DTYPE_CODE[dtype] + D
+    pp = workloads.gen_normal((N_PP, 2, P, H, D), seed0 + 1, dtype, DEV)
+    sp = workloads.gen_normal((N_SP, 2, SPS, H, D), seed0 + 2, dtype, DEV)
+    q_all = workloads.gen_normal((MAX_Q, H, D), seed0 + 3, dtype, DEV)
+    rng = np.random.default_rng(seed0)
+    pid = rng.permutation(N_PP).astype(np.int32)
+    sid = rng.permutation(N_SP).astype(np.int32)
+    pid_d = torch.from_numpy(pid).to(DEV)
+    sid_d = torch.from_numpy(sid).to(DEV)
+    pp_h, sp_h = pp.double().cpu().numpy(), sp.double().cpu().numpy()
+    q_h = q_all.double().cpu().numpy()
+    stream = torch.cuda.current_stream().cuda_stream
+    worst = 0.0
+    n = 0
+    for n_pp, n_st in KV_CASES:
+        # visible rows in table order: whole patch pages, then special tokens
+        k_rows = [pp_h[p, 0] for p in pid[:n_pp]] + [sp_h[s, 0] for s in sid]
+        v_rows = [pp_h[p, 1] for p in pid[:n_pp]] + [sp_h[s, 1] for s in sid]
+        kv = n_pp * P + n_st
+        K = np.concatenate(k_rows)[:kv]
+        V = np.concatenate(v_rows)[:kv]
+        for tq in TQ_CASES:
+            ref = dense_attention(q_h[:tq], K, V)
+            q = q_all[:tq].contiguous()
+            for splits in SPLITS:
+                cfg = _config(dtype, D, splits)
+                ws = torch.empty(lbm.lbm_query_sizes(cfg)[2], dtype=torch.uint8, device=DEV)
+                out = torch.full_like(q, float("nan"))
+                lbm.lbm_paged_attention(cfg, q.data_ptr(), out.data_ptr(), tq, pp.data_ptr(),
+                                        sp.data_ptr(), pid_d.data_ptr(), n_pp, sid_d.data_ptr(),
+                                        n_st, ws.data_ptr(), stream)
+                torch.cuda.synchronize()
+                st = compare(out.double().cpu().numpy(), ref, dtype,
+                             f"{dtype} D={D} kv={kv} tq={tq} splits={splits}")
+                worst = max(worst, st["max_abs"])
+                n += 1
+        say(f"{dtype} D={D}: kv={kv} done ({n} cases), worst max-abs {worst:.3e}")
+
+
+def test_empty_visible_set_is_rejected():
+    cfg = _config("bf16", 64, 0)
+    ws = torch.empty(lbm.lbm_query_sizes(cfg)[2], dtype=torch.uint8, device=DEV)
+    q = torch.zeros(4, H, 64, dtype=torch.bfloat16, device=DEV)
+    out = torch.empty_like(q)
+    ids = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pool = torch.zeros(1, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(lbm.LbmError) as e:
+        lbm.lbm_paged_attention(cfg, q.data_ptr(), out.data_ptr(), 4, pool.data_ptr(),
+                                pool.data_ptr(), ids.data_ptr(), 0, ids.data_ptr(), 0,
+                                ws.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert e.value.name == "LBM_ERR_INVALID_ARG"
