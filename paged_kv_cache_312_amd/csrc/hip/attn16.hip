@@ -33,14 +33,17 @@
 //    address, so the loop does no page arithmetic;
 //  * online softmax in fp32 with exp2 and the scale folded into Q, against a
 //    running max that the score MFMAs subtract themselves (their accumulators
-//    start from -max) and that is refreshed (O rescaled, the tile's scores
+//    start from -max) and that is refreshed (O rescaled, the block's scores
 //    recomputed from LDS) only when a weight would exceed 256; row sums by
 //    16-bit dot products of the rounded weights;
+//  * each tile in two 32-key blocks, in the order K Q^T (block 0), K Q^T
+//    (block 1) beside block 0's exponentials, P V (block 0) beside block 1's
+//    exponentials, P V (block 1), with the order pinned, so that the vector
+//    ALU and the matrix cores of a SIMD work at the same time;
 //  * O^T += V^T P^T on the same MFMA with P taken from registers (no LDS trip),
 //    P rounded to the input type (round to nearest even); the V operand comes from the
 //    row-major tile through gfx950's LDS transpose reads;
-//  * 226 VGPRs and no scratch, two workgroups per CU: a second workgroup
-//    on each SIMD overlaps one wavefront's exponentials with the other's MFMAs;
+//  * 218 VGPRs and no scratch, two workgroups per CU;
 //  * with several splits, each writes (O, m, l) partials that a separate merge
 //    kernel combines (a kernel boundary orders them: no fences, which on this
 //    chip would write back and invalidate the XCD's L2 that the workgroups
@@ -351,131 +354,213 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   float l_run[2] = {0.f, 0.f};
   const h2 ones = {static_cast<T>(1.0f), static_cast<T>(1.0f)};
 
-  // S^T[key][row] - m of tile position i for both halves, in base-2 units:
-  // lane holds row l32 (+32h) and keys kb*32 + 8j + 4hh + u (element 4j + u
-  // of s[h][kb]); each K operand read feeds both halves' MFMAs.  Each
-  // accumulator starts from -m_run in every element, so the MFMAs subtract
-  // the running max themselves; the start is written into the accumulator's
-  // own registers each tile (the asm keeps the compiler from carrying a
-  // broadcast copy of -m across the loop, which would cost 16 registers per
-  // half).  On the split's last tile, keys past the visible set are masked.
-  auto scores = [&](int32_t i, bool last, f32x16 (*s)[2]) __attribute__((always_inline)) {
-    const uint16_t* K = lds_k[i & (NST - 1)];
+  // S^T[key][row] - m of key block kb (keys 32kb .. 32kb+31) of a tile, for
+  // both halves, in base-2 units: lane holds row l32 (+32h) and keys
+  // 32kb + 8j + 4hh + u (element 4j + u of s[h][kb]); each K operand read
+  // feeds both halves' MFMAs.  Each accumulator starts from -m_run in every
+  // element, so the MFMAs subtract the running max themselves.
+  // -m_run in every element of s[h][kb] (the asm keeps the compiler from
+  // carrying a broadcast copy across the loop, 16 registers per half)
+  auto start_block = [&](int kb, f32x16 (*s)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       float nm = -m_run[h];
       asm volatile("" : "+v"(nm));
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[h][kb][e] = nm;
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const h8 kf = *reinterpret_cast<const h8*>(K + k_row + kb * 32 * LS +
-                                                   (((2 * ks + hh) ^ k_x) * 8));
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          s[h][kb] = Elt<T>::mfma(kf, qf[h][ks], s[h][kb]);
-      }
-    if (last) {
-      const int32_t lim = a.kv_len - (t_begin + i) * 64 - 4 * hh;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            s[h][kb][e] = kb * 32 + 8 * (e >> 2) + (e & 3) >= lim ? -INFINITY : s[h][kb][e];
+      for (int e = 0; e < 16; ++e) s[h][kb][e] = nm;
     }
   };
-  // p = 2^(s - shift) in T, grouped as the B operand of the PV MFMA (group
-  // G = 2kb + g holds elements 8g..8g+7 of s[kb]); returns this lane's sum of
-  // the rounded p (exactly the weights the PV product uses).
-  auto exponentiate = [&](const f32x16* s, float shift, h8* pb) __attribute__((always_inline)) {
-    float lt[2] = {0.f, 0.f};
+  auto qk_block = [&](const uint16_t* K, int kb, f32x16 (*s)[2]) __attribute__((always_inline)) {
+    start_block(kb, s);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int ks = 0; ks < 4; ++ks) {
+      const h8 kf = *reinterpret_cast<const h8*>(K + k_row + kb * 32 * LS +
+                                                 (((2 * ks + hh) ^ k_x) * 8));
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        s[h][kb] = Elt<T>::mfma(kf, qf[h][ks], s[h][kb]);
+    }
+  };
+  // on the split's last tile, keys of block kb past the visible set
+  auto mask_block = [&](int32_t i, int kb, f32x16 (*s)[2]) __attribute__((always_inline)) {
+    const int32_t lim = a.kv_len - (t_begin + i) * 64 - 4 * hh;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        s[h][kb][e] = kb * 32 + 8 * (e >> 2) + (e & 3) >= lim ? -INFINITY : s[h][kb][e];
+  };
+  // p = 2^(s - shift[h]) of key block kb in T, grouped as the B operand of the
+  // PV MFMA (group G = 2kb + g holds elements 8g..8g+7 of s[h][kb]); lt[h]
+  // receives this lane's sum of the rounded p (exactly the weights the PV
+  // product uses)
+  auto exp_block = [&](const f32x16 (*s)[2], int kb, const float* shift, h8 (*pb)[4], float* lt)
+                       __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      lt[h] = 0.f;
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         h8 v;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = static_cast<T>(fast_exp2(s[kb][8 * g + u] - shift));
+        for (int u = 0; u < 8; ++u) v[u] = static_cast<T>(fast_exp2(s[h][kb][8 * g + u] - shift[h]));
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const h2 pr = {v[2 * u], v[2 * u + 1]};
-          lt[kb] = Elt<T>::dot2(pr, ones, lt[kb]);
+          lt[h] = Elt<T>::dot2(pr, ones, lt[h]);
         }
-        pb[2 * kb + g] = v;
-      }
-    return lt[0] + lt[1];
-  };
-  // the row's tile max minus m_run (both lanes of the row agree)
-  auto row_max = [&](const f32x16* s) __attribute__((always_inline)) {
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-    return fmaxf(mx, __shfl_xor(mx, 32));
-  };
-
-  // One tile: scores, weights, and O += P V for both halves.  Softmax runs
-  // against the running max as it stands (the scores arrive with it
-  // subtracted).  On the split's first tile the max is the tile's own, so the
-  // largest weight is 1 and the row sum never underflows; afterwards the max
-  // is raised only when some lane's weights would sum past 256 (a jump of
-  // the max), and then that tile's scores are recomputed from the stage
-  // (still resident until the step's barrier), O and l rescaled and the
-  // weights redone.  Any max not below the true one gives the same quotient,
-  // since numerator and denominator share it.
-  auto tile = [&](int32_t i, bool first, bool last) __attribute__((always_inline)) {
-    f32x16 s[2][2];
-    h8 pb[2][4];
-    float lt[2] = {0.f, 0.f};
-    scores(i, last, s);
-    if (first) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float mx = row_max(s[h]);
-        m_run[h] = mx;
-        lt[h] = exponentiate(s[h], mx, pb[h]);
-      }
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) lt[h] = exponentiate(s[h], 0.f, pb[h]);
-      if (__ballot(!(lt[0] <= 256.f) || !(lt[1] <= 256.f))) {
-        scores(i, last, s);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float step_up = fmaxf(row_max(s[h]), 0.f);
-          const float alpha = fast_exp2(-step_up);
-          l_run[h] *= alpha;
-#pragma unroll
-          for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) o[h][db][e] *= alpha;
-          lt[h] = exponentiate(s[h], step_up, pb[h]);
-          m_run[h] += step_up;
-        }
+        pb[h][2 * kb + g] = v;
       }
     }
-    l_run[0] += lt[0];
-    l_run[1] += lt[1];
-    // O^T[d][row] += V^T[d][keys] P^T[keys][row]; each V operand read feeds
-    // both halves' MFMAs
-    const uint16_t* V = lds_v[i & (NST - 1)];
+  };
+  // four of exp_block's weights: elements 4q .. 4q+3 of s[h][kb], added to lt
+  auto exp_part = [&](const f32x16 (*s)[2], int h, int kb, int q, h8 (*pb)[4], float* lt)
+                      __attribute__((always_inline)) {
+    h8& v = pb[h][2 * kb + (q >> 1)];
+    const int o4 = 4 * (q & 1);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[o4 + u] = static_cast<T>(fast_exp2(s[h][kb][4 * q + u]));
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const h2 pr = {v[o4 + 2 * u], v[o4 + 2 * u + 1]};
+      lt[h] = Elt<T>::dot2(pr, ones, lt[h]);
+    }
+  };
+  // O^T[d][row] += V^T[d][keys] P^T[keys][row] over key block kb; each V
+  // operand read feeds both halves' MFMAs
+  auto pv_block = [&](const uint16_t* V, int kb, const h8 (*pb)[4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int G = 0; G < 4; ++G) {
+      for (int G = 2 * kb; G < 2 * kb + 2; ++G) {
         const uint16_t* p = V + (db == 0 ? v_rd0 : v_rd1) + (16 * G) * LS;
         const h8 vf = v_operand<h8>(p, p + 8 * LS);
 #pragma unroll
         for (int h = 0; h < 2; ++h) o[h][db] = Elt<T>::mfma(vf, pb[h][G], o[h][db]);
       }
+  };
+  // the row's max over key blocks kb0 .. kb1 minus m_run (both lanes of the
+  // row agree)
+  auto row_max = [&](const f32x16* s, int kb0, int kb1) __attribute__((always_inline)) {
+    float mx = s[kb0][0];
+    for (int kb = kb0; kb <= kb1; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+    return fmaxf(mx, __shfl_xor(mx, 32));
+  };
+  // raise half h's running max by step_up (>= 0): O and l scale by 2^-step_up
+  auto raise_max = [&](int h, float step_up) __attribute__((always_inline)) {
+    const float alpha = fast_exp2(-step_up);
+    l_run[h] *= alpha;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[h][db][e] *= alpha;
+    m_run[h] += step_up;
+  };
+  // One tile: scores, weights, and O += P V for both halves, by key block so
+  // that each block's exponentials run beside the other block's MFMAs: K Q^T
+  // of block 0; K Q^T of block 1 beside block 0's weights; P V of block 0
+  // beside block 1's weights; P V of block 1.  Softmax runs against the
+  // running max as it stands (the scores arrive with it subtracted).  On the
+  // split's first tile the max is the tile's own, so the largest weight is 1
+  // and the row sum never underflows; afterwards the max is raised only when
+  // some lane's weights of a block would sum past 256 (a jump of the max):
+  // then the block's scores are recomputed from the stage (resident until the
+  // step's barrier), O and l rescaled and the block's weights redone (a jump
+  // in block 0 also shifts block 1's scores; one in block 1 finds block 0's
+  // terms already in O, which the rescale carries to the new max).  Any max
+  // not below the true one gives the same quotient, since numerator and
+  // denominator share it.
+  auto tile = [&](int32_t i, bool first, bool last) __attribute__((always_inline)) {
+    const uint16_t* K = lds_k[i & (NST - 1)];
+    const uint16_t* V = lds_v[i & (NST - 1)];
+    f32x16 s[2][2];
+    h8 pb[2][4];
+    float lt0[2], lt1[2];
+    qk_block(K, 0, s);
+    if (last) mask_block(i, 0, s);
+    if (first) {
+      qk_block(K, 1, s);
+      if (last) mask_block(i, 1, s);
+      float mx[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        mx[h] = row_max(s[h], 0, 1);
+        m_run[h] = mx[h];
+      }
+      exp_block(s, 0, mx, pb, lt0);
+      exp_block(s, 1, mx, pb, lt1);
+    } else {
+      // block 1's K Q^T MFMAs, each followed by four of block 0's weights
+      // (the fences pin the order, so the vector ALU works while the matrix
+      // cores do)
+      h8 kf1[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kf1[ks] = *reinterpret_cast<const h8*>(K + k_row + 32 * LS + (((2 * ks + hh) ^ k_x) * 8));
+      lt0[0] = lt0[1] = 0.f;
+      start_block(1, s);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const int ks = st >> 1, h = st & 1;
+        s[h][1] = Elt<T>::mfma(kf1[ks], qf[h][ks], s[h][1]);
+        exp_part(s, st >> 2, 0, st & 3, pb, lt0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (last) mask_block(i, 1, s);
+      if (__ballot(!(lt0[0] <= 256.f) || !(lt0[1] <= 256.f))) {
+        qk_block(K, 0, s);
+        if (last) mask_block(i, 0, s);
+        float su[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          su[h] = fmaxf(row_max(s[h], 0, 0), 0.f);
+          raise_max(h, su[h]);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[h][1][e] -= su[h];
+        }
+        exp_block(s, 0, su, pb, lt0);
+      }
+      l_run[0] += lt0[0];
+      l_run[1] += lt0[1];
+      // block 0's P V MFMAs, each after four of block 1's weights
+      h8 vf0[4];
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int G = 0; G < 2; ++G) {
+          const uint16_t* p = V + (db == 0 ? v_rd0 : v_rd1) + (16 * G) * LS;
+          vf0[2 * db + G] = v_operand<h8>(p, p + 8 * LS);
+        }
+      lt1[0] = lt1[1] = 0.f;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const int db = st >> 2, G = (st >> 1) & 1, h = st & 1;
+        exp_part(s, st >> 2, 1, st & 3, pb, lt1);
+        o[h][db] = Elt<T>::mfma(vf0[2 * db + G], pb[h][G], o[h][db]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (__ballot(!(lt1[0] <= 256.f) || !(lt1[1] <= 256.f))) {
+        qk_block(K, 1, s);
+        if (last) mask_block(i, 1, s);
+        float su[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          su[h] = fmaxf(row_max(s[h], 1, 1), 0.f);
+          raise_max(h, su[h]);
+        }
+        exp_block(s, 1, su, pb, lt1);
+      }
+      l_run[0] += lt1[0];
+      l_run[1] += lt1[1];
+      pv_block(V, 1, pb);
+      return;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) l_run[h] += lt0[h] + lt1[h];
+    pv_block(V, 0, pb);
+    pv_block(V, 1, pb);
   };
 
   // Prologue: row codes of positions 0 .. 2kLead-1, then K and V of
