@@ -14,6 +14,10 @@ namespace lbm {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// staging registers of the K/V loads: a native vector (HIP's float4 is a
+// struct, whose copies between address spaces keep the staging arrays in
+// scratch memory)
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // TR: a skip-append step, whose keys [tr_start, kv_len) are the frame's own rows
 template <int D, bool TR>
@@ -85,8 +89,8 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const BatchArgs b) {
   const int lc = tid % CPR;
   const int lk = tid / CPR;
   const int32_t col_off = (head * D + lc * 4) * 4;
-  float4 kreg[PASSES], vreg[PASSES];
-  auto load_tile = [&](int32_t t) {
+  f32x4 kreg[PASSES], vreg[PASSES];
+  auto load_tile = [&](int32_t t) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < PASSES; ++r) {
       const char *kp, *vp;
@@ -97,16 +101,16 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const BatchArgs b) {
         kp = static_cast<const char*>(a.tk) + off;
         vp = static_cast<const char*>(a.tv) + off;
       }
-      kreg[r] = *reinterpret_cast<const float4*>(kp);
-      vreg[r] = *reinterpret_cast<const float4*>(vp);
+      kreg[r] = *reinterpret_cast<const f32x4*>(kp);
+      vreg[r] = *reinterpret_cast<const f32x4*>(vp);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < PASSES; ++r) {
       const int key = r * KPP + lk;
-      *reinterpret_cast<float4*>(&lds_k[buf][key * KS + lc * 4]) = kreg[r];
-      *reinterpret_cast<float4*>(&lds_v[buf][key * VS + lc * 4]) = vreg[r];
+      *reinterpret_cast<f32x4*>(&lds_k[buf][key * KS + lc * 4]) = kreg[r];
+      *reinterpret_cast<f32x4*>(&lds_v[buf][key * VS + lc * 4]) = vreg[r];
     }
   };
 
