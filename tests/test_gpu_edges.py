@@ -98,3 +98,80 @@ def test_empty_visible_set_is_rejected():
                                 pool.data_ptr(), ids.data_ptr(), 0, ids.data_ptr(), 0,
                                 ws.data_ptr(), torch.cuda.current_stream().cuda_stream)
     assert e.value.name == "LBM_ERR_INVALID_ARG"
+
+
+# (tile, key within the tile) of the planted score jumps: block 0 and block 1
+# of inner tiles, a second, larger jump later in the same row, and the last
+# (masked) tile
+JUMPS = [(3, 5), (5, 40), (7, 50), (9, 0), (11, 33), (12, 2)]
+
+
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 64), ("f16", 64), ("f32", 64)])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_running_max_jumps(dtype, head_dim, splits):
+    """Rows whose scores jump far above the running max inside key block 0
+    or block 1 of a tile (the kernels' rescale paths), once or twice per row,
+    on inner tiles and on the last, partly masked tile; compared with dense
+    attention (the oracle) over the same rows.  A planted key dominates its
+    row, whose output is then that key's V row, so V is drawn at 1/4 scale:
+    the outputs stay in the range of the workload's averaged ones, for which
+    the fp16 and bf16 bounds are set."""
+    D = head_dim
+    n_pp, n_st = 7, 91                    # 791 keys: 12 full tiles and a 23-key tail
+    kv = n_pp * P + n_st
+    seed0 = 9400 + 10 * DTYPE_CODE[dtype] + splits
+    pp = workloads.gen_normal((N_PP, 2, P, H, D), seed0 + 1, dtype, DEV)
+    sp = workloads.gen_normal((N_SP, 2, SPS, H, D), seed0 + 2, dtype, DEV)
+    tq = 96
+    q = workloads.gen_normal((tq, H, D), seed0 + 3, dtype, DEV)
+    pp[:, 1] *= 0.25
+    sp[:, 1] *= 0.25
+    rng = np.random.default_rng(seed0)
+    pid = rng.permutation(N_PP).astype(np.int32)
+    sid = rng.permutation(N_SP).astype(np.int32)
+
+    def slot(pos):
+        """(pool, page, token) of visible key position pos under the tables."""
+        if pos < n_pp * P:
+            return pp, int(pid[pos // P]), pos % P
+        j = pos - n_pp * P
+        return sp, int(sid[j // SPS]), j % SPS
+
+    # planted row j (query row 3j) jumps at JUMPS[j % 6] shifted by 2(j // 6),
+    # and, for even j, again at JUMPS[(j + 2) % 6] shifted by 2(j // 6) + 1
+    # with a larger score (no two plants share a key): K at that key is a
+    # multiple of the row's query for head j % H, placing its score ~20 (first)
+    # or ~43 (second) log2 units above the unplanted ones
+    for j, r in enumerate(range(0, tq, 3)):
+        h = j % H
+        qr = q[r, h].float()
+        plants = [(JUMPS[j % 6], 2 * (j // 6), 14.0)]
+        if j % 2 == 0:
+            plants.append((JUMPS[(j + 2) % 6], 2 * (j // 6) + 1, 30.0))
+        for (t, k), off, score in plants:
+            pos = t * 64 + k + off
+            assert pos < kv
+            pool, page, tok = slot(pos)
+            gain = score / float((qr * qr).sum()) * (D ** 0.5)
+            pool[page, 0, tok, h] = (qr * gain).to(pool.dtype)
+    pp_h, sp_h, q_h = pp.double().cpu().numpy(), sp.double().cpu().numpy(), q.double().cpu().numpy()
+    K = np.concatenate([pp_h[p, 0] for p in pid[:n_pp]] + [sp_h[s, 0] for s in sid])[:kv]
+    V = np.concatenate([pp_h[p, 1] for p in pid[:n_pp]] + [sp_h[s, 1] for s in sid])[:kv]
+    ref = dense_attention(q_h, K, V)
+    cfg = _config(dtype, D, splits)
+    ws = torch.empty(lbm.lbm_query_sizes(cfg)[2], dtype=torch.uint8, device=DEV)
+    out = torch.full_like(q, float("nan"))
+    pid_d = torch.from_numpy(pid).to(DEV)   # kept alive until the launch has run
+    sid_d = torch.from_numpy(sid).to(DEV)
+    lbm.lbm_paged_attention(cfg, q.data_ptr(), out.data_ptr(), tq, pp.data_ptr(), sp.data_ptr(),
+                            pid_d.data_ptr(), n_pp, sid_d.data_ptr(), n_st, ws.data_ptr(),
+                            torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    # the planted keys dominate their rows (a weight of 2^14 or more against
+    # the rest), which the test checks so that it exercises what it claims
+    s = np.einsum("qhd,khd->qhk", q_h, K) / np.sqrt(D) * np.log2(np.e)
+    lead = [s[r, j % H].max() - np.partition(s[r, j % H], -2)[-2]
+            for j, r in enumerate(range(0, tq, 3))]
+    assert min(lead) > 8.0, f"planted jumps too small: {min(lead):.1f}"
+    st = compare(out.double().cpu().numpy(), ref, dtype, f"{dtype} jumps splits={splits}")
+    say(f"{dtype} splits={splits}: max-abs {st['max_abs']:.3e}, smallest lead {min(lead):.1f}")
