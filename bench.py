@@ -167,8 +167,11 @@ def pmc_summary(fetch_dir, write_dir):
 def measure_stream(cfg, dev, steps, warmup, splits_req=0, keep=False, skip_steps=0):
     """Stream ``cfg`` through its first step and the window fill, ``warmup``
     more steps, then time ``steps`` frame steps (all blocks: append, evict and
-    plan once, attention), with HIP events around every lbm_run and every
-    append of one further step; then ``skip_steps`` skip-append frames (each
+    plan once, attention), with HIP events around one lbm_run per step (block
+    i mod B of step i: every block's launch has the same shape within a step,
+    and an event pair at every launch would itself add ~6 us of queue work per
+    event to the steps being timed) and around every append of one further
+    step; then ``skip_steps`` skip-append frames (each
     frame's queries over the visible set and its own rows, nothing stored).
     Returns the figures (and, with ``keep``, the live cache and inputs for the
     CPU baseline)."""
@@ -190,18 +193,18 @@ def measure_stream(cfg, dev, steps, warmup, splits_req=0, keep=False, skip_steps
     out_init = torch.empty((cfg.initial_frames * T, H, D), dtype=cache.dtype, device=dev)
     torch.cuda.synchronize()
 
-    def frame_step(inputs, out_bufs, nq, ev=None):
+    def frame_step(inputs, out_bufs, nq, ev=None, ev_block=-1):
         for b in range(B):
             q, k, v = inputs[b]
             cache.append_frame(b, k, v)
             if b == 0:
                 cache.evict_frames()
                 cache.plan(nq)
-            if ev is not None:
-                ev[b][0].record(stream)
+            if b == ev_block:
+                ev[0].record(stream)
             cache.run(b, q, out_bufs[b])
-            if ev is not None:
-                ev[b][1].record(stream)
+            if b == ev_block:
+                ev[1].record(stream)
 
     frame_step(init, [out_init] * B, cfg.initial_frames * T)
     F = cfg.initial_frames
@@ -217,15 +220,15 @@ def measure_stream(cfg, dev, steps, warmup, splits_req=0, keep=False, skip_steps
     torch.cuda.synchronize()
     F_first = F + 1
 
-    # timed region: K steps; attention launches bracketed by events on the
-    # launch stream for the roofline figure
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in range(B)] for _ in range(steps)]
+    # timed region: K steps; one attention launch per step bracketed by events
+    # on the launch stream for the roofline figure
+    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+          for _ in range(steps)]
     kv_lens = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        frame_step(sets[step_idx % N_INPUT_SETS], outs, T, ev[i])
+        frame_step(sets[step_idx % N_INPUT_SETS], outs, T, ev[i], i % B)
         F += 1
         step_idx += 1
         kv_lens.append(cache.get_plan()[0] if i == 0 else kv_lens[-1] + cfg.special_per_frame)
@@ -235,12 +238,11 @@ def measure_stream(cfg, dev, steps, warmup, splits_req=0, keep=False, skip_steps
     assert cache.stats()["frame_count"] == F
 
     attn_ms = 0.0
-    flops = 0.0
+    flops = 0.0          # algorithmic FLOPs of the bracketed launches
     for i in range(steps):
-        for b in range(B):
-            attn_ms += ev[i][b][0].elapsed_time(ev[i][b][1])
-        flops += B * 4.0 * T * kv_lens[i] * H * D
-    n_launch = steps * B
+        attn_ms += ev[i][0].elapsed_time(ev[i][1])
+        flops += 4.0 * T * kv_lens[i] * H * D
+    n_launch = steps
     avg_launch_ms = attn_ms / n_launch
     achieved_tflops = flops / (attn_ms * 1e-3) / 1e12
     ms_per_step = elapsed * 1e3 / steps
@@ -269,8 +271,8 @@ def measure_stream(cfg, dev, steps, warmup, splits_req=0, keep=False, skip_steps
     skip = None
     if skip_steps > 0:
         kv_cache = cache.get_plan()[0]
-        ev_s = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-                 for _ in range(B)] for _ in range(skip_steps)]
+        ev_s = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+                for _ in range(skip_steps)]
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         for i in range(skip_steps):
@@ -278,15 +280,17 @@ def measure_stream(cfg, dev, steps, warmup, splits_req=0, keep=False, skip_steps
             cache.plan_transient(T, T)
             for b in range(B):
                 q, k, v = inputs[b]
-                ev_s[i][b][0].record(stream)
+                if b == i % B:
+                    ev_s[i][0].record(stream)
                 cache.run_transient(b, q, k, v, outs[b])
-                ev_s[i][b][1].record(stream)
+                if b == i % B:
+                    ev_s[i][1].record(stream)
         torch.cuda.synchronize()
         el = time.perf_counter() - t1
-        s_ms = sum(e0.elapsed_time(e1) for row in ev_s for e0, e1 in row)
-        s_flops = skip_steps * B * 4.0 * T * (kv_cache + T) * H * D
+        s_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev_s)
+        s_flops = skip_steps * 4.0 * T * (kv_cache + T) * H * D
         skip = {"fps": skip_steps / el, "tflops": s_flops / (s_ms * 1e-3) / 1e12,
-                "avg_launch_ms": s_ms / (skip_steps * B), "kv_len": kv_cache + T}
+                "avg_launch_ms": s_ms / skip_steps, "kv_len": kv_cache + T}
         assert cache.stats()["frame_count"] == F + 1   # nothing appended by the skip frames
 
     res = {"fps": fps, "ms_per_step": ms_per_step, "tflops": achieved_tflops,
@@ -332,8 +336,9 @@ def measure_batch(cfg, dev, n_streams, steps, splits_req=0, n_sets=2):
         for f in range(cfg.scale_frames + cfg.sliding_window - cfg.initial_frames):
             append_all(si, sets[si][f % n_sets], T)
     torch.cuda.synchronize()
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in range(B)] for _ in range(steps)]
+    # one batched launch per step bracketed by events (block i mod B of step i)
+    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+          for _ in range(steps)]
     flops = 0.0
     t0 = time.perf_counter()
     for i in range(steps):
@@ -344,20 +349,22 @@ def measure_batch(cfg, dev, n_streams, steps, splits_req=0, n_sets=2):
                 if b == 0:
                     caches[si].evict_frames()
                     caches[si].plan(T)
-            ev[i][b][0].record(stream)
+            if b == i % B:
+                ev[i][0].record(stream)
             lbm.PagedKVCache.run_batch(caches, b, [sets[si][i % n_sets][b][0]
                                                    for si in range(n_streams)],
                                        [outs[si][b] for si in range(n_streams)])
-            ev[i][b][1].record(stream)
-        flops += sum(B * 4.0 * T * c.get_plan()[0] * H * D for c in caches)
+            if b == i % B:
+                ev[i][1].record(stream)
+        flops += sum(4.0 * T * c.get_plan()[0] * H * D for c in caches)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    attn_ms = sum(e0.elapsed_time(e1) for row in ev for e0, e1 in row)
+    attn_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev)
     F = caches[0].stats()["frame_count"]
     for c in caches:
         c.close()
     return {"fps": n_streams * steps / elapsed, "tflops": flops / (attn_ms * 1e-3) / 1e12,
-            "avg_launch_ms": attn_ms / (steps * B), "F_last": F}
+            "avg_launch_ms": attn_ms / steps, "F_last": F}
 
 
 def measure_graph(cfg, dev, steps, n_sets=N_INPUT_SETS):
