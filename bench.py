@@ -43,7 +43,8 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--splits", type=int, default=0, help="force the key-range split count")
     ap.add_argument("--variant-steps", type=int, default=100,
-                    help="timed steps of the same workload in fp16 (reported under 'variants')")
+                    help="timed steps of the fp16 and the no-scale-frames variants of the workload "
+                         "(reported under 'variants')")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--graph-steps", type=int, default=100,
                     help="frame steps replayed as HIP graphs (reported under 'variants')")
@@ -504,6 +505,17 @@ def main():
             "timed_frames": [v["F_first"], v["F_last"]],
             "attention_tflops": round(v["tflops"], 2),
             "frac": round(v["tflops"] / PEAK_FP16_TFLOPS, 4), "peak": PEAK_FP16_TFLOPS,
+            "avg_launch_ms": round(v["avg_launch_ms"], 4), "key_splits": v["splits"]}
+        # the eviction call's include_scale_frames=False: no frame kept beyond
+        # the window, so 8 fewer patch pages in the visible set
+        v = measure_stream(cfg.replace(scale_frames=0), dev, args.variant_steps, args.warmup,
+                           args.splits)
+        result["variants"]["no_scale_frames_bf16"] = {
+            "value": round(v["fps"], 3), "unit": "frames/s", "steps": args.variant_steps,
+            "timed_frames": [v["F_first"], v["F_last"]],
+            "kv_len": [v["kv_lens"][0], v["kv_lens"][-1]],
+            "attention_tflops": round(v["tflops"], 2),
+            "frac": round(v["tflops"] / PEAK_BF16_TFLOPS, 4), "peak": PEAK_BF16_TFLOPS,
             "avg_launch_ms": round(v["avg_launch_ms"], 4), "key_splits": v["splits"]}
 
     if not args.no_variants and args.graph_steps > 0:
