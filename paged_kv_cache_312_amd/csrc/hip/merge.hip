@@ -6,7 +6,10 @@
 // w_s = 2^(m_s - M), M = max_s m_s -- the usual combination of online-softmax
 // partials (each O_s and l_s is relative to its own m_s; maxima are kept in
 // base-2 exponent units, i.e. raw scores times log2(e)/sqrt(D)).
-// Memory-bound: one thread per 4 output columns of one (row, head).
+// Memory-bound: one thread per 4 output columns of one (row, head), which
+// issues the loads of up to eight splits' partials together and then combines
+// them (a loop that loaded one split per iteration would wait out one memory
+// latency per split).
 #include "attn_common.h"
 
 namespace lbm {
@@ -14,27 +17,52 @@ namespace {
 
 template <typename OutT, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
-  constexpr int CPR = D / 4;  // float4 chunks per (row, head)
+  constexpr int CPR = D / 4;    // float4 chunks per (row, head)
+  constexpr int kBatch = 8;     // splits loaded together
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t total = int64_t(a.Tq) * a.H * CPR;
   if (idx >= total) return;
   const int32_t chunk = int32_t(idx % CPR);
   const int64_t rh = idx / CPR;  // (row, head) = row * H + head
   const size_t split_stride = size_t(a.rows_pad) * a.H;
-  float M = -INFINITY;
-  for (int32_t s = 0; s < a.num_splits; ++s)
-    M = fmaxf(M, a.part_ml[(s * split_stride + rh) * 2]);
+  // M: the largest m_s so far; den and acc are relative to it.  A split
+  // without keys has m = -inf, l = 0, O = 0 and weighs 0.
+  float M = -INFINITY, den = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float den = 0.f;
-  for (int32_t s = 0; s < a.num_splits; ++s) {
-    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + (s * split_stride + rh) * 2);
-    const float w = fast_exp2(ml.x - M);
-    den += w * ml.y;
-    const float4 o = *reinterpret_cast<const float4*>(a.part_o + (s * split_stride + rh) * D + chunk * 4);
-    acc.x += w * o.x;
-    acc.y += w * o.y;
-    acc.z += w * o.z;
-    acc.w += w * o.w;
+  for (int32_t s0 = 0; s0 < a.num_splits; s0 += kBatch) {
+    float2 ml[kBatch];
+    float4 o[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const size_t srh = size_t(s0 + j) * split_stride + size_t(rh);
+      if (s0 + j < a.num_splits) {
+        ml[j] = *reinterpret_cast<const float2*>(a.part_ml + srh * 2);
+        o[j] = *reinterpret_cast<const float4*>(a.part_o + srh * D + chunk * 4);
+      } else {
+        ml[j] = make_float2(-INFINITY, 0.f);
+        o[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    float Mb = M;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) Mb = fmaxf(Mb, ml[j].x);
+    if (Mb == -INFINITY) continue;  // no keys in any split so far
+    const float r = fast_exp2(M - Mb);  // 0 while M is still -inf
+    den *= r;
+    acc.x *= r;
+    acc.y *= r;
+    acc.z *= r;
+    acc.w *= r;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float w = fast_exp2(ml[j].x - Mb);
+      den += w * ml[j].y;
+      acc.x += w * o[j].x;
+      acc.y += w * o[j].y;
+      acc.z += w * o[j].z;
+      acc.w += w * o[j].w;
+    }
+    M = Mb;
   }
   const float inv = 1.f / den;
   OutT* op = reinterpret_cast<OutT*>(a.out) + rh * D + chunk * 4;
