@@ -260,10 +260,12 @@ void lbm_graph_destroy(lbm_graph* graph);
 /* Stateless paged attention over caller-given tables (device int32 arrays):
  * the visible keys are the n_patch_pages patch pages listed in patch_ids
  * (each P tokens) followed by the first n_special_tokens tokens of the
- * special pages listed in special_ids.  Pools, q, out as above; the
- * workspace is a device buffer sized by lbm_query_sizes(cfg) (scratch for the
- * row table and split partials; no initial contents required).  Enqueues two
- * to three kernels on hip_stream. */
+ * special pages listed in special_ids.  Pools, q, out as above (16-byte
+ * aligned); the workspace is a 256-byte aligned device buffer sized by
+ * lbm_query_sizes(cfg) (scratch for the row table and split partials; no
+ * initial contents required).  Every id must lie below max_patch_pages or
+ * max_special_pages: the ids live on the device and are not checked here.
+ * Enqueues two to three kernels on hip_stream. */
 lbm_status lbm_paged_attention(const lbm_config* cfg, const void* q, void* out,
                                int32_t num_q_tokens, const void* patch_pool,
                                const void* special_pool, const int32_t* patch_ids,

@@ -577,6 +577,10 @@ lbm_status lbm_paged_attention(const lbm_config* cfg, const void* q, void* out,
   if ((st = kernel_supported(*cfg)) != LBM_OK) return st;
   if (!q || !out || !workspace || !aligned16(q) || !aligned16(out))
     return fail(LBM_ERR_INVALID_ARG, "q/out/workspace null or misaligned");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(LBM_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  if ((patch_pool && !aligned16(patch_pool)) || (special_pool && !aligned16(special_pool)))
+    return fail(LBM_ERR_INVALID_ARG, "pool not 16-byte aligned");
   if (num_q_tokens < 1 || num_q_tokens > cfg->max_q_tokens)
     return fail(LBM_ERR_INVALID_ARG, "num_q_tokens %d outside 1..%d", num_q_tokens,
                 cfg->max_q_tokens);

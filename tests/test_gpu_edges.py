@@ -100,6 +100,25 @@ def test_empty_visible_set_is_rejected():
     assert e.value.name == "LBM_ERR_INVALID_ARG"
 
 
+def test_misaligned_buffers_are_rejected():
+    """A workspace off 256-byte alignment, or a pool off 16, is refused before
+    any launch."""
+    cfg = _config("bf16", 64, 0)
+    ws = torch.empty(lbm.lbm_query_sizes(cfg)[2] + 256, dtype=torch.uint8, device=DEV)
+    q = torch.zeros(4, H, 64, dtype=torch.bfloat16, device=DEV)
+    out = torch.empty_like(q)
+    ids = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pool = torch.zeros(64, dtype=torch.bfloat16, device=DEV)
+    st = torch.cuda.current_stream().cuda_stream
+    for ws_ptr, pool_ptr in ((ws.data_ptr() + 64, pool.data_ptr()),
+                             (ws.data_ptr(), pool.data_ptr() + 8)):
+        with pytest.raises(lbm.LbmError) as e:
+            lbm.lbm_paged_attention(cfg, q.data_ptr(), out.data_ptr(), 4, pool_ptr, pool_ptr,
+                                    ids.data_ptr(), 1, ids.data_ptr(), 0, ws_ptr, st)
+        assert e.value.name == "LBM_ERR_INVALID_ARG"
+        assert "aligned" in str(e.value)
+
+
 # (tile, key within the tile) of the planted score jumps: block 0 and block 1
 # of inner tiles, a second, larger jump later in the same row, and the last
 # (masked) tile
