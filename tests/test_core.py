@@ -68,6 +68,18 @@ def test_core_matches_reference_no_scale_frames():
     assert st["scale_pages"] == 0 and st["live_pages"] == 64
 
 
+@pytest.mark.parametrize("kw", [dict(special_per_frame=0), dict(sliding_window=0),
+                                dict(scale_frames=0, sliding_window=1, initial_frames=1)],
+                         ids=["no_special", "no_window", "window1_no_scale"])
+def test_core_matches_reference_degenerate_configs(kw):
+    """No special tokens, no window, a one-frame window without scale frames;
+    with rejected frames rolled back."""
+    cfg = workloads.get_config(0).replace(total_frames=40, reject_prob=0.3, **kw)
+    acc = workloads.accept_draws(cfg)
+    assert not all(acc)
+    _lockstep(cfg, accept=acc)
+
+
 def test_core_matches_reference_long_stream():
     """10,000 frames: ~9,900 evictions and 3,750 special pages."""
     core, ref = _lockstep(workloads.get_config(3), check_every=61)

@@ -25,6 +25,10 @@ ODD_F16 = ODD_BF16.replace(name="odd_f16", cid=15, dtype="f16")
 # include_scale_frames=False of the pages' eviction call: no frame is kept
 # beyond the window (scale_frames = 0)
 ODD_NO_SCALE = ODD_BF16.replace(name="odd_no_scale", cid=16, scale_frames=0)
+# degenerate settings: no special tokens (an empty special stream), no window
+# (each frame's patches leave at its own step's eviction)
+ODD_NO_SPECIAL = ODD_BF16.replace(name="odd_no_special", cid=17, special_per_frame=0)
+ODD_NO_WINDOW = ODD_BF16.replace(name="odd_no_window", cid=18, sliding_window=0)
 
 
 def test_tiny_config_every_output():
@@ -33,7 +37,8 @@ def test_tiny_config_every_output():
 
 
 @pytest.mark.parametrize("splits", [0, 1, 3])
-@pytest.mark.parametrize("cfg", [ODD_BF16, ODD_F16, ODD_F32, ODD_F32_D32, ODD_NO_SCALE],
+@pytest.mark.parametrize("cfg", [ODD_BF16, ODD_F16, ODD_F32, ODD_F32_D32, ODD_NO_SCALE,
+                                 ODD_NO_SPECIAL, ODD_NO_WINDOW],
                          ids=lambda c: c.name)
 def test_small_streams_every_output(cfg, splits):
     w = run_stream(cfg, num_splits=splits, label=f"{cfg.name}/splits={splits}")

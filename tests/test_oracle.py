@@ -389,6 +389,26 @@ def test_stream_oracle_tiny_with_rejects_vs_brute():
     assert worst <= 1e-12
 
 
+# Degenerate settings of the method: no special tokens (the special stream
+# stays empty), no window (only the scale frames' patches and the specials
+# stay visible; each later frame's patches leave at its own step's eviction),
+# and a one-frame window without scale frames.
+DEGENERATE = {
+    "no_special": dict(special_per_frame=0),
+    "no_window": dict(sliding_window=0),
+    "window1_no_scale": dict(scale_frames=0, sliding_window=1, initial_frames=1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DEGENERATE))
+def test_stream_oracle_degenerate_configs_vs_brute(name):
+    cfg = workloads.get_config(0).replace(name=f"tiny_{name}", total_frames=14, reject_prob=0.3,
+                                          **DEGENERATE[name])
+    acc = workloads.accept_draws(cfg)
+    worst = _tiny_stream_vs_brute(cfg, accept=acc)
+    assert worst <= 1e-12
+
+
 def _tiny_oracle_after(cfg, n_steps):
     """Stream oracle of block 0 after the first n_steps steps of cfg."""
     orc = StreamOracle(cfg.patches_per_frame, cfg.special_per_frame, cfg.scale_frames,
