@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PEAK_FP16_TFLOPS = 2516.6      # MI355X dense fp16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X dense fp32 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 N_INPUT_SETS = 8
 
@@ -46,6 +47,8 @@ def parse():
                     help="timed steps of the fp16 and the no-scale-frames variants of the workload "
                          "(reported under 'variants')")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--f32-steps", type=int, default=20,
+                    help="timed steps of the fp32 (force_fp32) variant (reported under 'variants')")
     ap.add_argument("--graph-steps", type=int, default=100,
                     help="frame steps replayed as HIP graphs (reported under 'variants')")
     ap.add_argument("--batch-streams", type=int, default=4,
@@ -70,16 +73,19 @@ KERNEL_SOURCES = ["paged_kv_cache_312_amd/csrc/hip/attn16.hip",
                   "paged_kv_cache_312_amd/csrc/hip/attn_common.h",
                   "paged_kv_cache_312_amd/csrc/hip/merge.hip",
                   "paged_kv_cache_312_amd/csrc/hip/kernels.h"]
+APPEND_SOURCES = ["paged_kv_cache_312_amd/csrc/hip/append.hip",
+                  "paged_kv_cache_312_amd/csrc/hip/kernels.h"]
 COPY_BYTES = 1 << 30
 
 
-def kernel_source_hash(root: str = ROOT) -> str:
-    """Hash of the attention and merge sources with comments and blank space
-    removed (a comment edit does not change the kernel)."""
+def kernel_source_hash(root: str = ROOT, sources=None) -> str:
+    """Hash of the attention and merge sources (or of ``sources``) with
+    comments and blank space removed (a comment edit does not change the
+    kernel)."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in (KERNEL_SOURCES if sources is None else sources):
         with open(os.path.join(root, rel)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -88,17 +94,31 @@ def kernel_source_hash(root: str = ROOT) -> str:
     return h.hexdigest()[:16]
 
 
+def _traffic_record():
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            return json.loads(f.read().split("\n", 1)[1])
+    except (OSError, ValueError, IndexError):
+        return None
+
+
 def recorded_traffic():
     """Bytes per lbm_run from the traffic record, or None if it is missing or
     was measured on other kernel sources."""
-    try:
-        with open(TRAFFIC_RECORD) as f:
-            rec = json.loads(f.read().split("\n", 1)[1])
-    except (OSError, ValueError, IndexError):
-        return None
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    rec = _traffic_record()
+    if rec is None or rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_lbm_run")
+
+
+def recorded_append_traffic():
+    """HBM bytes of one single-frame append (K and V rows of one block) from
+    the traffic record, or None if it is missing or was measured on other
+    append sources."""
+    rec = _traffic_record()
+    if rec is None or rec.get("append_source_hash") != kernel_source_hash(sources=APPEND_SOURCES):
+        return None
+    return rec.get("hbm_bytes_per_append")
 
 
 def bf16_kernel(name: str, base: str) -> bool:
@@ -137,12 +157,15 @@ def pmc_summary(fetch_dir, write_dir):
         # the fill steps, at other shapes
         attn = [per[i][1] for i in ids if bf16_kernel(per[i][0], "attn_d64_kernel")][-72:]
         merge = [per[i][1] for i in ids if bf16_kernel(per[i][0], "merge_kernel")][-72:]
+        # the single-frame appends of the same three steps
+        app = [per[i][1] for i in ids if "append_scatter_kernel" in per[i][0]][-72:]
         copy = [per[i][1] for i in ids if "elementwise" in per[i][0]][-3:]
         if not attn or len(copy) < 3:
             raise SystemExit(f"{counter}: attention or calibration dispatches missing")
         out[counter] = {"attn_kib": statistics.mean(attn),
                         "merge_kib": statistics.mean(merge) if merge else 0.0,
                         "merges_per_attn": len(merge) / len(attn),
+                        "append_kib": statistics.mean(app) if app else None,
                         "copy_kib": statistics.mean(copy)}
     f, w = out["FETCH_SIZE"], out["WRITE_SIZE"]
     f_scale = COPY_BYTES / (f["copy_kib"] * 1024.0)
@@ -154,9 +177,16 @@ def pmc_summary(fetch_dir, write_dir):
            "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
            "raw_kib": out, "copy_bytes": COPY_BYTES}
+    if f["append_kib"] is not None and w["append_kib"] is not None:
+        a_fetch = f["append_kib"] * 1024.0 * f_scale
+        a_write = w["append_kib"] * 1024.0 * w_scale
+        rec.update(append_source_hash=kernel_source_hash(sources=APPEND_SOURCES),
+                   hbm_bytes_per_append=round(a_fetch + a_write),
+                   append_fetch_bytes=round(a_fetch), append_write_bytes=round(a_write))
     os.makedirs(os.path.dirname(TRAFFIC_RECORD), exist_ok=True)
     with open(TRAFFIC_RECORD, "w") as fh:
-        fh.write("HBM traffic of one lbm_run (attention + merge), 24-block ViT-L step; written by "
+        fh.write("HBM traffic of one lbm_run (attention + merge) and of one single-frame "
+                 "append, 24-block ViT-L step; written by "
                  "'bench.py --pmc-summary' from two rocprofv3 --pmc runs of 'bench.py --steps 2 "
                  "--warmup 0 --no-cpu-baseline --no-variants --calibrate-copy' (FETCH_SIZE, "
                  "then WRITE_SIZE)\n")
@@ -487,6 +517,7 @@ def main():
                      "flops_per_launch_avg": flops / n_launch},
         "append": {"bound": "hbm", "achieved": round(append_gbps, 1), "peak": PEAK_HBM_GBPS,
                    "unit": "GB/s", "frac": round(append_gbps / PEAK_HBM_GBPS, 4),
+                   "traffic": recorded_append_traffic(),
                    "avg_launch_ms": round(app_ms, 5), "bytes_per_launch": app_bytes},
     }
 
@@ -520,6 +551,19 @@ def main():
             "attention_tflops": round(v["tflops"], 2),
             "frac": round(v["tflops"] / PEAK_BF16_TFLOPS, 4), "peak": PEAK_BF16_TFLOPS,
             "avg_launch_ms": round(v["avg_launch_ms"], 4), "key_splits": v["splits"]}
+
+        # the force_fp32 path (fp32 storage, fp32 MFMA products and softmax)
+        # against the fp32 dense MFMA peak; a short timed run
+        if args.f32_steps > 0:
+            v = measure_stream(cfg.replace(dtype="f32"), dev, args.f32_steps, args.warmup,
+                               args.splits)
+            result["variants"]["fp32"] = {
+                "value": round(v["fps"], 3), "unit": "frames/s", "steps": args.f32_steps,
+                "timed_frames": [v["F_first"], v["F_last"]],
+                "attention_tflops": round(v["tflops"], 2),
+                "frac": round(v["tflops"] / PEAK_FP32_TFLOPS, 4), "peak": PEAK_FP32_TFLOPS,
+                "avg_launch_ms": round(v["avg_launch_ms"], 4), "key_splits": v["splits"],
+                "append_gbps": round(v["append_gbps"], 1)}
 
     if not args.no_variants and args.graph_steps > 0:
         gr = measure_graph(cfg, dev, args.graph_steps)

@@ -70,3 +70,21 @@ def test_traffic_is_reported_only_for_the_recorded_kernels(tmp_path, monkeypatch
 ])
 def test_bf16_kernel_names(name, base, want):
     assert bench.bf16_kernel(name, base) is want
+
+
+def test_append_traffic_follows_the_append_sources(tmp_path, monkeypatch):
+    """The append's recorded bytes are reported while append.hip and
+    kernels.h hash to the recorded value, and null otherwise (an attention
+    change alone does not void them)."""
+    import json
+    rec = {"kernel_source_hash": "0" * 16, "hbm_bytes_per_lbm_run": 1,
+           "append_source_hash": bench.kernel_source_hash(sources=bench.APPEND_SOURCES),
+           "hbm_bytes_per_append": 11534336}
+    path = tmp_path / "record.txt"
+    path.write_text("header\n" + json.dumps(rec))
+    monkeypatch.setattr(bench, "TRAFFIC_RECORD", str(path))
+    assert bench.recorded_append_traffic() == 11534336
+    assert bench.recorded_traffic() is None
+    path.write_text("header\n" + json.dumps(dict(rec, append_source_hash="1" * 16)))
+    assert bench.recorded_append_traffic() is None
+    assert bench.kernel_source_hash(sources=bench.APPEND_SOURCES) != bench.kernel_source_hash()
