@@ -32,10 +32,11 @@
 //  * per-step row table (one code per key position) gives each K/V row's
 //    address, so the loop does no page arithmetic;
 //  * online softmax in fp32 with exp2 and the scale folded into Q, against a
-//    running max that the score MFMAs subtract themselves (their accumulators
-//    start from -max) and that is refreshed (O rescaled, the block's scores
-//    recomputed from LDS) only when a weight would exceed 256; row sums by
-//    16-bit dot products of the rounded weights;
+//    running max that the score MFMAs subtract themselves (each chain starts
+//    with an MFMA over a bias column that holds -max; the max stays on the
+//    input type's grid, so the bias is exact) and that is refreshed (O
+//    rescaled, the block's scores recomputed from LDS) only when a weight
+//    would exceed 256; row sums by 16-bit dot products of the rounded weights;
 //  * each tile in two 32-key blocks, in the order K Q^T (block 0), K Q^T
 //    (block 1) beside block 0's exponentials, P V (block 0) beside block 1's
 //    exponentials, P V (block 1), with the order pinned, so that the vector
@@ -43,7 +44,7 @@
 //  * O^T += V^T P^T on the same MFMA with P taken from registers (no LDS trip),
 //    P rounded to the input type (round to nearest even); the V operand comes from the
 //    row-major tile through gfx950's LDS transpose reads;
-//  * 218 VGPRs and no scratch, two workgroups per CU;
+//  * 236-242 VGPRs and no scratch, two workgroups per CU;
 //  * with several splits, each writes (O, m, l) partials that a separate merge
 //    kernel combines (a kernel boundary orders them: no fences, which on this
 //    chip would write back and invalidate the XCD's L2 that the workgroups
@@ -150,6 +151,20 @@ __device__ __forceinline__ V8 v_operand(const uint16_t* p0, const uint16_t* p1) 
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
   const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(V8, both);
+}
+
+// The least value of type T that is >= x, as a float (the running max is kept
+// on T's grid, so that the score MFMAs can subtract it exactly).
+template <typename T>
+__device__ __forceinline__ float round_up_to(float x) {
+  const T t = static_cast<T>(x);  // nearest
+  float y = static_cast<float>(t);
+  if (y < x) {  // one unit in the last place towards +inf
+    uint16_t bits = __builtin_bit_cast(uint16_t, t);
+    bits = y >= 0.f ? uint16_t(bits + 1) : uint16_t(bits - 1);
+    y = static_cast<float>(__builtin_bit_cast(T, bits));
+  }
+  return y;
 }
 
 // one kernel per element type: attn_d64_kernel<__bf16> and attn_d64_kernel<_Float16>;
@@ -357,18 +372,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   // S^T[key][row] - m of key block kb (keys 32kb .. 32kb+31) of a tile, for
   // both halves, in base-2 units: lane holds row l32 (+32h) and keys
   // 32kb + 8j + 4hh + u (element 4j + u of s[h][kb]); each K operand read
-  // feeds both halves' MFMAs.  Each accumulator starts from -m_run in every
-  // element, so the MFMAs subtract the running max themselves.
-  // -m_run in every element of s[h][kb] (the asm keeps the compiler from
-  // carrying a broadcast copy across the loop, 16 registers per half)
+  // feeds both halves' MFMAs.  The chain starts with one more MFMA over a
+  // bias column: the key side holds 1 and the query side -m_run at
+  // contraction index 0 (lanes 0..31 hold indices 0..7 of both operands), so
+  // the accumulators start from -m_run without a move per element; m_run stays
+  // on T's grid, so the bias is exact.
+  h8 abias = {};
+  if (hh == 0) abias[0] = static_cast<T>(1.0f);
+  h8 bbias[2];
+  auto set_bias = [&](int h) __attribute__((always_inline)) {
+    bbias[h] = h8{};
+    if (hh == 0) bbias[h][0] = static_cast<T>(-m_run[h]);
+  };
+  set_bias(0);
+  set_bias(1);
   auto start_block = [&](int kb, f32x16 (*s)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float nm = -m_run[h];
-      asm volatile("" : "+v"(nm));
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[h][kb][e] = nm;
-    }
+    for (int h = 0; h < 2; ++h) s[h][kb] = Elt<T>::mfma(abias, bbias[h], f32x16{});
   };
   auto qk_block = [&](const uint16_t* K, int kb, f32x16 (*s)[2]) __attribute__((always_inline)) {
     start_block(kb, s);
@@ -448,15 +468,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
     return fmaxf(mx, __shfl_xor(mx, 32));
   };
-  // raise half h's running max by step_up (>= 0): O and l scale by 2^-step_up
-  auto raise_max = [&](int h, float step_up) __attribute__((always_inline)) {
+  // raise half h's running max by at least step_up (>= 0), to the next value
+  // on T's grid; step_up receives the raise taken.  O and l scale by
+  // 2^-step_up.
+  auto raise_max = [&](int h, float& step_up) __attribute__((always_inline)) {
+    const float m_new = round_up_to<T>(m_run[h] + step_up);
+    step_up = m_new - m_run[h];  // exact: both on T's grid
     const float alpha = fast_exp2(-step_up);
     l_run[h] *= alpha;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[h][db][e] *= alpha;
-    m_run[h] += step_up;
+    m_run[h] = m_new;
+    set_bias(h);
   };
   // One tile: scores, weights, and O += P V for both halves, by key block so
   // that each block's exponentials run beside the other block's MFMAs: K Q^T
@@ -483,14 +508,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     if (first) {
       qk_block(K, 1, s);
       if (last) mask_block(i, 1, s);
-      float mx[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        mx[h] = row_max(s[h], 0, 1);
-        m_run[h] = mx[h];
+        m_run[h] = round_up_to<T>(row_max(s[h], 0, 1));
+        set_bias(h);
       }
-      exp_block(s, 0, mx, pb, lt0);
-      exp_block(s, 1, mx, pb, lt1);
+      exp_block(s, 0, m_run, pb, lt0);
+      exp_block(s, 1, m_run, pb, lt1);
     } else {
       // block 1's K Q^T MFMAs, each followed by four of block 0's weights
       // (the fences pin the order, so the vector ALU works while the matrix
@@ -501,6 +525,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
         kf1[ks] = *reinterpret_cast<const h8*>(K + k_row + 32 * LS + (((2 * ks + hh) ^ k_x) * 8));
       lt0[0] = lt0[1] = 0.f;
       start_block(1, s);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         const int ks = st >> 1, h = st & 1;
