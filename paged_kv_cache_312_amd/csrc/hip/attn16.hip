@@ -198,7 +198,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   const int32_t split = grp - head * a.num_splits;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // wavefront-uniform (an SGPR), so the LDS addresses of the loads are scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int32_t HD = a.H * D;
   const int32_t t_begin = split * a.tiles_per_split;
