@@ -270,12 +270,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   // loads land only in stages that are never read again, which keeps the
   // steady-state step free of branches
   auto tile_at = [&](int32_t x) __attribute__((always_inline)) { return t_begin + min(x, n_t - 1); };
+  // this lane's column of a K or V row in either pool, as lane constants in
+  // VGPRs: a row address is then one select of a base and one add per load
+  const char* col_base[2][2] = {
+      {static_cast<const char*>(a.patch_pool) + k_col,
+       static_cast<const char*>(a.patch_pool) + v_col + a.vstride_patch},
+      {static_cast<const char*>(a.special_pool) + k_col,
+       static_cast<const char*>(a.special_pool) + v_col + a.vstride_special}};
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) asm volatile("" : "+v"(col_base[p][kv]));
   auto row_ptr = [&](uint32_t code, bool v) __attribute__((always_inline)) {
     const bool special = (code >> 31) != 0;
-    const char* base = special ? static_cast<const char*>(a.special_pool)
-                               : static_cast<const char*>(a.patch_pool);
-    const int32_t off = v ? v_col + (special ? a.vstride_special : a.vstride_patch) : k_col;
-    return base + (code & 0x7fffffffu) + off;
+    const char* base = special ? col_base[1][v] : col_base[0][v];
+    return base + (code & 0x7fffffffu);
   };
   // K and V of tile position x into stage x mod NST.  Skip-append step: keys
   // in [tr_start, kv_len) come from the frame's own rows (the row table holds
