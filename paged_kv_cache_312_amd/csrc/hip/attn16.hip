@@ -44,7 +44,7 @@
 //  * O^T += V^T P^T on the same MFMA with P taken from registers (no LDS trip),
 //    P rounded to the input type (round to nearest even); the V operand comes from the
 //    row-major tile through gfx950's LDS transpose reads;
-//  * 236-242 VGPRs and no scratch, two workgroups per CU;
+//  * 238-240 VGPRs and no scratch, two workgroups per CU;
 //  * with several splits, each writes (O, m, l) partials that a separate merge
 //    kernel combines (a kernel boundary orders them: no fences, which on this
 //    chip would write back and invalidate the XCD's L2 that the workgroups
