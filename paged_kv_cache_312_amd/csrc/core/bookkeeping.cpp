@@ -292,9 +292,9 @@ void Bookkeeping::plan_record(std::vector<int32_t>* out) const {
 // ---------------------------------------------------------------------------
 
 int32_t choose_splits(int32_t num_q_tokens, int32_t kv_len, int32_t num_heads, int32_t num_cu,
-                      int32_t wg_per_cu, int32_t split_cap, int32_t forced) {
+                      int32_t wg_per_cu, int32_t split_cap, int32_t forced, int32_t rows_per_wg) {
   if (num_q_tokens < 1 || kv_len < 1 || num_heads < 1 || num_cu < 1 || wg_per_cu < 1 ||
-      split_cap < 1)
+      split_cap < 1 || rows_per_wg < 1)
     return LBM_ERR_INVALID_ARG;
   const int32_t n_tiles = ceil_div(kv_len, kKeysPerTile);
   const int32_t cap = std::min({split_cap, kSplitMax, n_tiles});
@@ -304,7 +304,8 @@ int32_t choose_splits(int32_t num_q_tokens, int32_t kv_len, int32_t num_heads, i
   };
   if (forced > 0) return normalise(std::min(forced, cap));
   // Cost model, in tile-times of one workgroup alone on a CU, fitted to the
-  // 16-bit kernel (256 query rows per workgroup) on MI355X: k workgroups
+  // 16-bit kernel (256 query rows per workgroup) on MI355X and applied to
+  // either kernel's workgroups (the fp32 kernel's hold 128 rows): k workgroups
   // sharing a CU each take 1 + 0.85 (k - 1) per tile (a second workgroup
   // mostly hides latency; the CU's throughput grows little); every workgroup
   // pays a start/finish cost of about 2 tiles; splitting adds a merge pass (a
@@ -312,7 +313,7 @@ int32_t choose_splits(int32_t num_q_tokens, int32_t kv_len, int32_t num_heads, i
   // workgroups are dispatched in rounds of num_cu * wg_per_cu; the last,
   // partial round spreads its workgroups over the CUs.
   constexpr double kShare = 0.85, kFixed = 2.0, kMergeLaunch = 13.0, kMergePerSplit = 4.0;
-  const int64_t units = int64_t(ceil_div(num_q_tokens, kRowsPerGroup)) * num_heads;
+  const int64_t units = int64_t(ceil_div(num_q_tokens, rows_per_wg)) * num_heads;
   const int64_t slots = int64_t(num_cu) * wg_per_cu;
   auto per_tile = [&](int64_t k) { return 1.0 + kShare * double(k - 1); };
   int32_t best = 1;

@@ -54,6 +54,11 @@ static lbm_status hip_fail(hipError_t e, const char* what) {
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// query rows of one workgroup of the attention kernel for `dtype`
+static int32_t kernel_rows_per_wg(int32_t dtype) {
+  return dtype == LBM_F32 ? kRowsPerWGf32 : kRowsPerWG16;
+}
+
 }  // namespace lbm
 
 using namespace lbm;
@@ -176,8 +181,7 @@ lbm_status launch_attention_batch(const lbm_config& c, AttnArgs* as, int32_t n, 
   std::memset(&b, 0, sizeof(b));
   b.n = n;
   for (int32_t i = 0; i < n; ++i) {
-    finish_attn_args(&as[i], c.head_dim, splits,
-                     c.dtype == LBM_F32 ? kRowsPerWGf32 : kRowsPerWG16);
+    finish_attn_args(&as[i], c.head_dim, splits, kernel_rows_per_wg(c.dtype));
     b.s[i] = as[i];
     b.item_start[i + 1] = b.item_start[i] + as[i].total_items;
   }
@@ -426,7 +430,8 @@ lbm_status plan_impl(lbm_cache* c, int32_t num_q_tokens, int32_t own, void* hip_
 
   const int32_t cap = split_capacity(c->ws, num_q_tokens);
   int32_t ns = choose_splits(num_q_tokens, p.kv_len + own, c->cfg.num_heads, c->num_cu,
-                             c->wg_per_cu, cap, c->cfg.num_splits);
+                             c->wg_per_cu, cap, c->cfg.num_splits,
+                             kernel_rows_per_wg(c->cfg.dtype));
   if (ns < 1) ns = 1;
   c->plan = p;
   c->plan_q = num_q_tokens;
@@ -553,14 +558,15 @@ lbm_status lbm_run_batch(lbm_cache* const* caches, int32_t n, int32_t block_idx,
                       c->workspace, c->ws);
     as[i].kv_len = c->plan.kv_len;
     as[i].tr_start = as[i].kv_len;
-    rows += int64_t(c->plan_q + kRowsPerGroup - 1) / kRowsPerGroup * kRowsPerGroup;
+    const int32_t rpw = kernel_rows_per_wg(c->cfg.dtype);
+    rows += int64_t(c->plan_q + rpw - 1) / rpw * rpw;
     kv_max = std::max(kv_max, c->plan.kv_len);
     cap = std::min(cap, split_capacity(c->ws, c->plan_q));
   }
   // one split count for the whole launch, chosen for the combined work
   int32_t ns = choose_splits(int32_t(std::min<int64_t>(rows, INT32_MAX)), kv_max,
                              c0->cfg.num_heads, c0->num_cu, c0->wg_per_cu, cap,
-                             c0->cfg.num_splits);
+                             c0->cfg.num_splits, kernel_rows_per_wg(c0->cfg.dtype));
   if (ns < 1) ns = 1;
   return launch_attention_batch(c0->cfg, as, n, ns, static_cast<hipStream_t>(hip_stream));
 }
@@ -610,7 +616,8 @@ lbm_status lbm_paged_attention(const lbm_config* cfg, const void* q, void* out,
     (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
   const int32_t ns = choose_splits(num_q_tokens, a.kv_len, cfg->num_heads, ncu,
                                    attn_occupancy(cfg->dtype, cfg->head_dim),
-                                   split_capacity(ws, num_q_tokens), cfg->num_splits);
+                                   split_capacity(ws, num_q_tokens), cfg->num_splits,
+                                   kernel_rows_per_wg(cfg->dtype));
   return launch_attention(*cfg, &a, ns < 1 ? 1 : ns, stream);
 }
 
@@ -762,7 +769,8 @@ lbm_status lbm_graph_create(lbm_cache* c, int32_t num_frames, const void* const*
   const int64_t kv_est = int64_t(c->cfg.scale_frames + c->cfg.sliding_window) *
                              c->cfg.patches_per_frame + c->bk.plan_info().special_tokens + nq;
   g->ns = choose_splits(nq, int32_t(std::min<int64_t>(kv_est, kMaxKvLen - 1)), c->cfg.num_heads,
-                        c->num_cu, c->wg_per_cu, split_capacity(c->ws, nq), c->cfg.num_splits);
+                        c->num_cu, c->wg_per_cu, split_capacity(c->ws, nq), c->cfg.num_splits,
+                        kernel_rows_per_wg(c->cfg.dtype));
   if (g->ns < 1) g->ns = 1;
   g->bytes = c->ws.special_ids_off + sizeof(int32_t) * size_t(std::max(1, c->cfg.max_special_pages)) -
              c->ws.desc_off;
