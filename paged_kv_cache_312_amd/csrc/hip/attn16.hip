@@ -44,7 +44,8 @@
 //  * O^T += V^T P^T on the same MFMA with P taken from registers (no LDS trip),
 //    P rounded to the input type (round to nearest even); the V operand comes from the
 //    row-major tile through gfx950's LDS transpose reads;
-//  * 238-240 VGPRs and no scratch, two workgroups per CU;
+//  * 242-246 VGPRs and no scratch, two workgroups per CU; the steady-state
+//    loop takes four steps per iteration, so LDS operand offsets are constants;
 //  * with several splits, each writes (O, m, l) partials that a separate merge
 //    kernel combines (a kernel boundary orders them: no fences, which on this
 //    chip would write back and invalidate the XCD's L2 that the workgroups
@@ -508,9 +509,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   // terms already in O, which the rescale carries to the new max).  Any max
   // not below the true one gives the same quotient, since numerator and
   // denominator share it.
-  auto tile = [&](int32_t i, bool first, bool last) __attribute__((always_inline)) {
-    const uint16_t* K = lds_k[i & (NST - 1)];
-    const uint16_t* V = lds_v[i & (NST - 1)];
+  auto tile = [&](int32_t i, bool first, bool last, int stage) __attribute__((always_inline)) {
+    const uint16_t* K = lds_k[stage];
+    const uint16_t* V = lds_v[stage];
     f32x16 s[2][2];
     h8 pb[2][4];
     float lt0[2], lt1[2];
@@ -622,17 +623,35 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     return;
   }
   if (n_t == 1) {
-    tile(0, true, true);
+    tile(0, true, true, 0);
   } else {
     step_loads(0);
-    tile(0, true, false);
+    tile(0, true, false, 0);
     end_step(0);
-    for (int32_t i = 1; i + 1 < n_t; ++i) {
+    // four steps per iteration, so that each tile's stage (i mod 4, with i = 1
+    // mod 4 at the top) is a constant and its LDS operand addresses fold into
+    // the instructions' offsets
+    int32_t i = 1;
+    for (; i + 4 < n_t; i += 4) {
       step_loads(i);
-      tile(i, false, false);
+      tile(i, false, false, 1);
+      end_step(i);
+      step_loads(i + 1);
+      tile(i + 1, false, false, 2);
+      end_step(i + 1);
+      step_loads(i + 2);
+      tile(i + 2, false, false, 3);
+      end_step(i + 2);
+      step_loads(i + 3);
+      tile(i + 3, false, false, 0);
+      end_step(i + 3);
+    }
+    for (; i + 1 < n_t; ++i) {
+      step_loads(i);
+      tile(i, false, false, i & (NST - 1));
       end_step(i);
     }
-    tile(n_t - 1, false, true);
+    tile(n_t - 1, false, true, (n_t - 1) & (NST - 1));
   }
 
   // loads of clamped positions may still be in flight: the workgroup's LDS
