@@ -44,7 +44,7 @@
 //  * O^T += V^T P^T on the same MFMA with P taken from registers (no LDS trip),
 //    P rounded to the input type (round to nearest even); the V operand comes from the
 //    row-major tile through gfx950's LDS transpose reads;
-//  * 242-246 VGPRs and no scratch, two workgroups per CU; the steady-state
+//  * 240-246 VGPRs and no scratch, two workgroups per CU; the steady-state
 //    loop takes four steps per iteration, so LDS operand offsets are constants;
 //  * with several splits, each writes (O, m, l) partials that a separate merge
 //    kernel combines (a kernel boundary orders them: no fences, which on this
