@@ -39,10 +39,12 @@ lbm_status lbmcore_dump(const lbmcore* core, int32_t* buf, int64_t cap, int64_t*
 lbm_status lbmcore_stats(const lbmcore* core, lbm_stats* out);
 
 /* The planner's key-range split choice for a run of num_q_tokens queries
- * over kv_len keys: returns the split count (>= 1), or a negative status. */
+ * over kv_len keys by a kernel whose workgroups hold rows_per_wg query rows
+ * (0: the 16-bit kernel's 256; the fp32 kernel's are 128): returns the split
+ * count (>= 1), or a negative status. */
 int32_t lbmcore_choose_splits(int32_t num_q_tokens, int32_t kv_len, int32_t num_heads,
                               int32_t num_cu, int32_t wg_per_cu, int32_t split_cap,
-                              int32_t forced);
+                              int32_t forced, int32_t rows_per_wg);
 
 const char* lbmcore_last_error(void);
 

@@ -416,9 +416,10 @@ class CoreBookkeeping:
         return s.as_dict()
 
     @staticmethod
-    def choose_splits(num_q_tokens, kv_len, num_heads, num_cu, wg_per_cu, split_cap, forced=0):
+    def choose_splits(num_q_tokens, kv_len, num_heads, num_cu, wg_per_cu, split_cap, forced=0,
+                      rows_per_wg=0):
         return core_lib().lbmcore_choose_splits(num_q_tokens, kv_len, num_heads, num_cu,
-                                                wg_per_cu, split_cap, forced)
+                                                wg_per_cu, split_cap, forced, rows_per_wg)
 
 
 class StepGraph:

@@ -114,8 +114,9 @@ lbm_status lbmcore_stats(const lbmcore* core, lbm_stats* out) {
 
 int32_t lbmcore_choose_splits(int32_t num_q_tokens, int32_t kv_len, int32_t num_heads,
                               int32_t num_cu, int32_t wg_per_cu, int32_t split_cap,
-                              int32_t forced) {
-  return lbm::choose_splits(num_q_tokens, kv_len, num_heads, num_cu, wg_per_cu, split_cap, forced);
+                              int32_t forced, int32_t rows_per_wg) {
+  return lbm::choose_splits(num_q_tokens, kv_len, num_heads, num_cu, wg_per_cu, split_cap, forced,
+                            rows_per_wg > 0 ? rows_per_wg : lbm::kRowsPerGroup);
 }
 
 const char* lbmcore_last_error(void) { return lbm::last_error(); }

@@ -236,15 +236,15 @@ void error_paths() {
   lbmcore_destroy(nullptr);
 
   // the planner's split choice over edge arguments
-  CHECK(lbmcore_choose_splits(0, 100, 16, 256, 2, 16, 0) < 0, "zero queries accepted");
-  CHECK(lbmcore_choose_splits(100, 0, 16, 256, 2, 16, 0) < 0, "zero keys accepted");
-  CHECK(lbmcore_choose_splits(1, 1, 1, 1, 1, 1, 0) == 1, "one key, one split");
+  CHECK(lbmcore_choose_splits(0, 100, 16, 256, 2, 16, 0, 0) < 0, "zero queries accepted");
+  CHECK(lbmcore_choose_splits(100, 0, 16, 256, 2, 16, 0, 0) < 0, "zero keys accepted");
+  CHECK(lbmcore_choose_splits(1, 1, 1, 1, 1, 1, 0, 0) == 1, "one key, one split");
   for (int32_t kv = 1; kv < 200000; kv = kv * 3 + 7)
     for (int32_t q = 1; q < 20000; q = q * 5 + 3) {
-      const int32_t n = lbmcore_choose_splits(q, kv, 16, 256, 2, 16, 0);
+      const int32_t n = lbmcore_choose_splits(q, kv, 16, 256, 2, 16, 0, (q & 1) ? 128 : 0);
       const int32_t tiles = (kv + 63) / 64;
       CHECK(n >= 1 && n <= 16 && n <= tiles, "splits %d for q %d kv %d", n, q, kv);
-      const int32_t f = lbmcore_choose_splits(q, kv, 16, 256, 2, 16, 1000);
+      const int32_t f = lbmcore_choose_splits(q, kv, 16, 256, 2, 16, 1000, 0);
       CHECK(f >= 1 && f <= 16 && f <= tiles, "forced splits %d for kv %d", f, kv);
     }
 }

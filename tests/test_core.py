@@ -211,3 +211,11 @@ def test_choose_splits():
     assert cs(22, 66, 2, 256, 3, 16, 8) == 2          # two tiles only
     assert cs(22, 66, 2, 256, 3, 16) >= 1
     assert cs(0, 66, 2, 256, 3, 16) < 0
+    # measured on MI355X at the ViT-L steady state (kv_len 99,054): 8 splits is
+    # the 16-bit kernel's best (256-row workgroups, two per CU), and the fp32
+    # kernel (128-row workgroups, two per CU) runs best at 10-16 against 8;
+    # the model, counting each kernel's own workgroups, picks 8 and 10
+    assert cs(1375, 99054, 16, 256, 2, 16) == 8
+    assert cs(1375, 99054, 16, 256, 2, 16, 0, 256) == 8
+    assert cs(1375, 99054, 16, 256, 2, 16, 0, 128) == 10
+    assert cs(1375, 99054, 16, 256, 2, 16, 0, -1) == 8   # non-positive: the 256-row default
