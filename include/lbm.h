@@ -272,6 +272,32 @@ lbm_status lbm_paged_attention(const lbm_config* cfg, const void* q, void* out,
                                int32_t n_patch_pages, const int32_t* special_ids,
                                int32_t n_special_tokens, void* workspace, void* hip_stream);
 
+/* lbm_paged_attention without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The row table and the split partials live
+ * in a static scratch array of 64 MiB in the library's device code, one copy
+ * per GPU, held from module load until the process ends; its device address
+ * is looked up once per device (hipGetSymbolAddress) on the first call there.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).  Limits: the row table takes 4 bytes per visible key, in whole
+ * 64-key tiles, and the scratch holds it for the largest visible set a valid
+ * config allows (2^24 keys); a visible set beyond the config's own maximum
+ * (scale_frames + sliding_window patch pages, max_special_pages special pages,
+ * max_q_tokens own rows) is refused with INVALID_ARG, as lbm_paged_attention
+ * refuses it.  The split count is capped to the partials that fit beside the
+ * row table (a single split needs none): 9 splits for 1375 query rows of 16
+ * heads, so a large run may split less than lbm_paged_attention would.  Every call on one GPU shares that
+ * GPU's scratch and leaves its contents behind (nothing in it needs to start
+ * at zero): calls that overlap on one GPU -- on different streams, or from
+ * different host threads without ordering -- race and give wrong results; the
+ * caller orders them.  Other arguments, results and errors as for
+ * lbm_paged_attention. */
+lbm_status lbm_paged_attention_static(const lbm_config* cfg, const void* q, void* out,
+                                      int32_t num_q_tokens, const void* patch_pool,
+                                      const void* special_pool, const int32_t* patch_ids,
+                                      int32_t n_patch_pages, const int32_t* special_ids,
+                                      int32_t n_special_tokens, void* hip_stream);
+
 /* The stats record ([P3] "Inspecting Cache Statistics"). */
 lbm_status lbm_get_stats(const lbm_cache* cache, lbm_stats* out);
 

@@ -22,7 +22,7 @@ __all__ = [
     "lbm_rollback_last_frame", "lbm_plan", "lbm_run", "lbm_plan_transient", "lbm_run_transient",
     "lbm_run_batch", "MAX_BATCH", "lbm_graph_create", "lbm_graph_launch", "lbm_graph_destroy",
     "lbm_graph_num_splits", "StepGraph",
-    "lbm_paged_attention", "lbm_get_stats",
+    "lbm_paged_attention", "lbm_paged_attention_static", "lbm_get_stats",
     "lbm_dump_state", "lbm_get_plan", "lbm_plan_num_splits", "lbm_last_error",
     "PagedKVCache", "CoreBookkeeping",
 ]
@@ -176,6 +176,18 @@ def lbm_paged_attention(cfg: LbmConfig, q: int, out: int, num_q_tokens: int, pat
                                   c_void_p(patch_ids), n_patch_pages, c_void_p(special_ids),
                                   n_special_tokens, c_void_p(workspace), c_void_p(stream)),
         "lbm_paged_attention")
+
+
+def lbm_paged_attention_static(cfg: LbmConfig, q: int, out: int, num_q_tokens: int,
+                               patch_pool: int, special_pool: int, patch_ids: int,
+                               n_patch_pages: int, special_ids: int, n_special_tokens: int,
+                               stream: int) -> None:
+    _ck(lib().lbm_paged_attention_static(byref(cfg), c_void_p(q), c_void_p(out), num_q_tokens,
+                                         c_void_p(patch_pool), c_void_p(special_pool),
+                                         c_void_p(patch_ids), n_patch_pages,
+                                         c_void_p(special_ids), n_special_tokens,
+                                         c_void_p(stream)),
+        "lbm_paged_attention_static")
 
 
 def lbm_get_stats(handle: int) -> dict:

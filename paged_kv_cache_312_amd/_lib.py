@@ -71,6 +71,9 @@ LBM_FUNCS = {
     "lbm_paged_attention": (c_int32, [POINTER(LbmConfig), c_void_p, c_void_p, c_int32, c_void_p,
                                       c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p,
                                       c_void_p]),
+    "lbm_paged_attention_static": (c_int32, [POINTER(LbmConfig), c_void_p, c_void_p, c_int32,
+                                             c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
+                                             c_int32, c_void_p]),
     "lbm_get_stats": (c_int32, [c_void_p, POINTER(LbmStats)]),
     "lbm_dump_state": (c_int32, [c_void_p, POINTER(c_int32), c_int64, POINTER(c_int64)]),
     "lbm_get_plan": (c_int32, [c_void_p, POINTER(c_int32), c_int64, POINTER(c_int64)]),

@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -29,12 +30,14 @@ int32_t attn_occupancy(int32_t dtype, int32_t head_dim) {
   return dtype == LBM_F32 ? attn_occupancy_f32(head_dim) : attn_occupancy16();
 }
 
+int32_t partial_rows(int32_t Tq) { return (Tq + kRowsPerGroup - 1) / kRowsPerGroup * kRowsPerGroup; }
+
 void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits, int32_t rows_per_wg) {
   a->n_tiles = (a->kv_len + kKeysPerTile - 1) / kKeysPerTile;
   a->tiles_per_split = (a->n_tiles + num_splits - 1) / num_splits;
   a->num_splits = (a->n_tiles + a->tiles_per_split - 1) / a->tiles_per_split;
   a->n_qt = (a->Tq + rows_per_wg - 1) / rows_per_wg;
-  a->rows_pad = (a->Tq + kRowsPerGroup - 1) / kRowsPerGroup * kRowsPerGroup;
+  a->rows_pad = partial_rows(a->Tq);
   a->total_items = a->n_qt * a->H * a->num_splits;
   a->items_per_xcd = (a->total_items + 7) / 8;
   a->scale_log2 = float(1.4426950408889634 / std::sqrt(double(head_dim)));
@@ -202,6 +205,122 @@ lbm_status launch_attention_batch(const lbm_config& c, AttnArgs* as, int32_t n, 
 
 lbm_status launch_attention(const lbm_config& c, AttnArgs* a, int32_t splits, hipStream_t st) {
   return launch_attention_batch(c, a, 1, splits, st);
+}
+
+}  // namespace
+
+// Scratch of lbm_paged_attention_static: the row table and the split partials
+// of one call, in device memory that the library never allocates at run time.
+// Each GPU holds its own copy from module load until the process ends.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+
+// Device address of `scratch` on each device, looked up once per device with
+// that device current (the host-side name `scratch` is not a device address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+lbm_status static_scratch(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "current device");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(LBM_ERR_UNSUPPORTED, "device %d beyond the %d the static scratch serves", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e, "static scratch address");
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return LBM_OK;
+}
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Stateless paged attention with the row table and split partials in `ws`:
+// a workspace laid out by workspace_layout(cfg) when ws_bytes is 0, else a
+// buffer of ws_bytes bytes laid out here for this call alone (row table, then
+// the partials of as many splits as fit).
+lbm_status paged_attention_impl(const lbm_config* cfg, const void* q, void* out,
+                                int32_t num_q_tokens, const void* patch_pool,
+                                const void* special_pool, const int32_t* patch_ids,
+                                int32_t n_patch_pages, const int32_t* special_ids,
+                                int32_t n_special_tokens, char* ws, size_t ws_bytes,
+                                void* hip_stream) {
+  if (!cfg) return fail(LBM_ERR_INVALID_ARG, "cfg is null");
+  lbm_status st = validate_config(*cfg);
+  if (st != LBM_OK) return st;
+  if ((st = kernel_supported(*cfg)) != LBM_OK) return st;
+  if (!q || !out || !aligned16(q) || !aligned16(out))
+    return fail(LBM_ERR_INVALID_ARG, "q/out null or misaligned");
+  if ((patch_pool && !aligned16(patch_pool)) || (special_pool && !aligned16(special_pool)))
+    return fail(LBM_ERR_INVALID_ARG, "pool not 16-byte aligned");
+  if (num_q_tokens < 1 || num_q_tokens > cfg->max_q_tokens)
+    return fail(LBM_ERR_INVALID_ARG, "num_q_tokens %d outside 1..%d", num_q_tokens,
+                cfg->max_q_tokens);
+  if (n_patch_pages < 0 || n_special_tokens < 0)
+    return fail(LBM_ERR_INVALID_ARG, "negative table size");
+  if (n_patch_pages > 0 && (!patch_pool || !patch_ids))
+    return fail(LBM_ERR_INVALID_ARG, "patch pool or ids null");
+  if (n_special_tokens > 0 && (!special_pool || !special_ids))
+    return fail(LBM_ERR_INVALID_ARG, "special pool or ids null");
+  const int64_t kv = int64_t(n_patch_pages) * cfg->patches_per_frame + n_special_tokens;
+  if (kv < 1 || kv >= kMaxKvLen) return fail(LBM_ERR_INVALID_ARG, "visible length %lld", (long long)kv);
+  const int64_t n_pos = (kv + kKeysPerTile - 1) / kKeysPerTile * kKeysPerTile;
+  uint32_t* rowtab = nullptr;
+  float* part_ml = nullptr;
+  float* part_o = nullptr;
+  int32_t cap = 1;
+  const WorkspaceLayout wl = workspace_layout(*cfg);
+  if (kv > wl.rowtab_len)
+    return fail(LBM_ERR_INVALID_ARG, "visible length %lld exceeds the config's %d",
+                (long long)kv, wl.rowtab_len);
+  if (ws_bytes == 0) {
+    rowtab = reinterpret_cast<uint32_t*>(ws + wl.rowtab_off);
+    part_ml = reinterpret_cast<float*>(ws + wl.part_ml_off);
+    part_o = reinterpret_cast<float*>(ws + wl.part_o_off);
+    cap = split_capacity(wl, num_q_tokens);
+  } else {
+    const size_t tab = align256(size_t(n_pos) * sizeof(uint32_t));
+    if (tab > ws_bytes)
+      return fail(LBM_ERR_INVALID_ARG,
+                  "visible length %lld needs a %zu-byte row table; the static scratch holds %zu",
+                  (long long)kv, tab, ws_bytes);
+    // one split's (m, l) and O rows; a single split writes no partials
+    const size_t rows = size_t(partial_rows(num_q_tokens)) * size_t(cfg->num_heads);
+    const size_t ml1 = rows * 2 * sizeof(float), o1 = rows * size_t(cfg->head_dim) * sizeof(float);
+    const size_t room = ws_bytes - tab;
+    int64_t fit = 0;
+    while (fit < kSplitMax && align256(size_t(fit + 1) * ml1) + align256(size_t(fit + 1) * o1) <= room)
+      ++fit;
+    cap = int32_t(std::max<int64_t>(1, fit));
+    rowtab = reinterpret_cast<uint32_t*>(ws);
+    part_ml = reinterpret_cast<float*>(ws + tab);
+    part_o = reinterpret_cast<float*>(ws + tab + align256(size_t(std::max<int64_t>(fit, 1)) * ml1));
+  }
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  st = launch_rowtab_for(*cfg, patch_ids, special_ids, n_patch_pages * cfg->patches_per_frame,
+                         int32_t(kv), 0, rowtab, stream);
+  if (st != LBM_OK) return st;
+  AttnArgs a = base_args(*cfg, q, out, num_q_tokens, patch_pool, special_pool, rowtab, ws,
+                         WorkspaceLayout());
+  a.part_ml = part_ml;
+  a.part_o = part_o;
+  a.kv_len = int32_t(kv);
+  a.tr_start = a.kv_len;
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  const int32_t ns = choose_splits(num_q_tokens, a.kv_len, cfg->num_heads, ncu,
+                                   attn_occupancy(cfg->dtype, cfg->head_dim), cap,
+                                   cfg->num_splits, kernel_rows_per_wg(cfg->dtype));
+  return launch_attention(*cfg, &a, ns < 1 ? 1 : ns, stream);
 }
 
 }  // namespace
@@ -577,48 +696,26 @@ lbm_status lbm_paged_attention(const lbm_config* cfg, const void* q, void* out,
                                int32_t n_patch_pages, const int32_t* special_ids,
                                int32_t n_special_tokens, void* workspace, void* hip_stream) {
   clear_error();
-  if (!cfg) return fail(LBM_ERR_INVALID_ARG, "cfg is null");
-  lbm_status st = validate_config(*cfg);
-  if (st != LBM_OK) return st;
-  if ((st = kernel_supported(*cfg)) != LBM_OK) return st;
-  if (!q || !out || !workspace || !aligned16(q) || !aligned16(out))
-    return fail(LBM_ERR_INVALID_ARG, "q/out/workspace null or misaligned");
+  if (!workspace) return fail(LBM_ERR_INVALID_ARG, "workspace is null");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(LBM_ERR_INVALID_ARG, "workspace not 256-byte aligned");
-  if ((patch_pool && !aligned16(patch_pool)) || (special_pool && !aligned16(special_pool)))
-    return fail(LBM_ERR_INVALID_ARG, "pool not 16-byte aligned");
-  if (num_q_tokens < 1 || num_q_tokens > cfg->max_q_tokens)
-    return fail(LBM_ERR_INVALID_ARG, "num_q_tokens %d outside 1..%d", num_q_tokens,
-                cfg->max_q_tokens);
-  if (n_patch_pages < 0 || n_special_tokens < 0)
-    return fail(LBM_ERR_INVALID_ARG, "negative table size");
-  if (n_patch_pages > 0 && (!patch_pool || !patch_ids))
-    return fail(LBM_ERR_INVALID_ARG, "patch pool or ids null");
-  if (n_special_tokens > 0 && (!special_pool || !special_ids))
-    return fail(LBM_ERR_INVALID_ARG, "special pool or ids null");
-  const int64_t kv = int64_t(n_patch_pages) * cfg->patches_per_frame + n_special_tokens;
-  if (kv < 1 || kv >= kMaxKvLen) return fail(LBM_ERR_INVALID_ARG, "visible length %lld", (long long)kv);
-  const WorkspaceLayout ws = workspace_layout(*cfg);
-  if (kv > ws.rowtab_len)
-    return fail(LBM_ERR_INVALID_ARG, "visible length %lld exceeds the config's %d",
-                (long long)kv, ws.rowtab_len);
-  char* wb = static_cast<char*>(workspace);
-  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  uint32_t* rowtab = reinterpret_cast<uint32_t*>(wb + ws.rowtab_off);
-  st = launch_rowtab_for(*cfg, patch_ids, special_ids, n_patch_pages * cfg->patches_per_frame,
-                         int32_t(kv), 0, rowtab, stream);
+  return paged_attention_impl(cfg, q, out, num_q_tokens, patch_pool, special_pool, patch_ids,
+                              n_patch_pages, special_ids, n_special_tokens,
+                              static_cast<char*>(workspace), 0, hip_stream);
+}
+
+lbm_status lbm_paged_attention_static(const lbm_config* cfg, const void* q, void* out,
+                                      int32_t num_q_tokens, const void* patch_pool,
+                                      const void* special_pool, const int32_t* patch_ids,
+                                      int32_t n_patch_pages, const int32_t* special_ids,
+                                      int32_t n_special_tokens, void* hip_stream) {
+  clear_error();
+  char* base = nullptr;
+  lbm_status st = static_scratch(&base);
   if (st != LBM_OK) return st;
-  AttnArgs a = base_args(*cfg, q, out, num_q_tokens, patch_pool, special_pool, rowtab, wb, ws);
-  a.kv_len = int32_t(kv);
-  a.tr_start = a.kv_len;
-  int dev = 0, ncu = 256;
-  if (hipGetDevice(&dev) == hipSuccess)
-    (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-  const int32_t ns = choose_splits(num_q_tokens, a.kv_len, cfg->num_heads, ncu,
-                                   attn_occupancy(cfg->dtype, cfg->head_dim),
-                                   split_capacity(ws, num_q_tokens), cfg->num_splits,
-                                   kernel_rows_per_wg(cfg->dtype));
-  return launch_attention(*cfg, &a, ns < 1 ? 1 : ns, stream);
+  return paged_attention_impl(cfg, q, out, num_q_tokens, patch_pool, special_pool, patch_ids,
+                              n_patch_pages, special_ids, n_special_tokens, base,
+                              kStaticScratchBytes, hip_stream);
 }
 
 lbm_status lbm_get_stats(const lbm_cache* c, lbm_stats* out) {

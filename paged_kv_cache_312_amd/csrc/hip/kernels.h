@@ -98,6 +98,10 @@ constexpr int32_t kRowsPerWG16 = kRowsPerGroup;
 constexpr int32_t kRowsPerWGf32 = 128;
 static_assert(kRowsPerGroup % kRowsPerWGf32 == 0, "partial rows cover both kernels' groups");
 
+// Rows of one split's partial-result block for Tq query rows (the kernels
+// index partials by query row; the block is padded to whole row groups).
+int32_t partial_rows(int32_t Tq);
+
 // Fill the split/grid fields of `a` for a launch (Tq, kv_len, splits known)
 // by a kernel with `rows_per_wg` query rows per workgroup.
 void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits, int32_t rows_per_wg);
