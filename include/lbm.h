@@ -246,9 +246,13 @@ lbm_status lbm_graph_create(lbm_cache* cache, int32_t num_frames, const void* co
  * plan, run (every block) with the graph's split count.  The caller fills
  * k/v/q before the launch (in stream order) and reads out after it.  The host
  * may run at most two steps ahead of the device (pinned staging in two
- * slots).  Errors: OUT_OF_PAGES, BAD_STATE (a step open and not every block
- * appended), HIP.  A HIP failure after the reservation leaves the
- * bookkeeping a step ahead of the pools. */
+ * slots).  The eviction is committed once the launch is enqueued.  Errors:
+ * OUT_OF_PAGES, BAD_STATE (a step open and not every block appended, or the
+ * cache left unusable by an earlier failure), HIP.  When the launch itself
+ * fails, a one-frame step's reservation is undone (the cache is as before the
+ * call); after a failed multi-frame step, or a failure once the step is
+ * queued, every step call (append, evict, rollback, plan, run, graph launch)
+ * returns BAD_STATE until lbm_cache_reset. */
 lbm_status lbm_graph_launch(lbm_graph* graph, void* hip_stream);
 
 /* The split count fixed at capture (0 for a null graph). */

@@ -82,6 +82,10 @@ struct lbm_cache {
   int32_t step_nf = 0;
   std::vector<uint8_t> appended;
 
+  // a failed multi-frame graph step left the bookkeeping ahead of the pools:
+  // every step call is refused until lbm_cache_reset
+  bool poisoned = false;
+
   // current plan
   bool plan_valid = false;
   uint64_t plan_epoch = 0;
@@ -118,6 +122,13 @@ namespace {
 
 lbm_status check_cache(const lbm_cache* c) {
   if (!c) return fail(LBM_ERR_INVALID_ARG, "cache is null");
+  return LBM_OK;
+}
+
+// check_cache, and the cache not left unusable by a failed step
+lbm_status check_live(const lbm_cache* c) {
+  if (!c) return fail(LBM_ERR_INVALID_ARG, "cache is null");
+  if (c->poisoned) return fail(LBM_ERR_BAD_STATE, "a failed step left the cache unusable; reset it");
   return LBM_OK;
 }
 
@@ -414,6 +425,7 @@ lbm_status lbm_cache_reset(lbm_cache* c) {
   c->bk.reset();
   c->step_open = false;
   c->plan_valid = false;
+  c->poisoned = false;
   return LBM_OK;
 }
 
@@ -433,7 +445,7 @@ lbm_status lbm_cache_seed_free_lists(lbm_cache* c, const int32_t* patch_order, i
 lbm_status lbm_append_frame(lbm_cache* c, int32_t block_idx, const void* k, const void* v,
                             int32_t num_frames, void* hip_stream) {
   clear_error();
-  lbm_status st = check_cache(c);
+  lbm_status st = check_live(c);
   if (st != LBM_OK) return st;
   if (block_idx < 0 || block_idx >= c->cfg.num_blocks)
     return fail(LBM_ERR_INVALID_ARG, "block_idx %d outside 0..%d", block_idx, c->cfg.num_blocks - 1);
@@ -485,7 +497,7 @@ lbm_status lbm_append_frame(lbm_cache* c, int32_t block_idx, const void* k, cons
 
 lbm_status lbm_evict_frames(lbm_cache* c, int32_t* evicted_ids, int32_t cap, int32_t* n_evicted) {
   clear_error();
-  lbm_status st = check_cache(c);
+  lbm_status st = check_live(c);
   if (st != LBM_OK) return st;
   if (cap > 0 && !evicted_ids) return fail(LBM_ERR_INVALID_ARG, "evicted_ids is null");
   std::vector<int32_t> ev;
@@ -498,7 +510,7 @@ lbm_status lbm_evict_frames(lbm_cache* c, int32_t* evicted_ids, int32_t cap, int
 
 lbm_status lbm_rollback_last_frame(lbm_cache* c) {
   clear_error();
-  lbm_status st = check_cache(c);
+  lbm_status st = check_live(c);
   if (st != LBM_OK) return st;
   st = c->bk.rollback();
   if (st != LBM_OK) return st;
@@ -565,7 +577,7 @@ lbm_status plan_impl(lbm_cache* c, int32_t num_q_tokens, int32_t own, void* hip_
 
 lbm_status lbm_plan(lbm_cache* c, int32_t num_q_tokens, void* hip_stream) {
   clear_error();
-  lbm_status st = check_cache(c);
+  lbm_status st = check_live(c);
   if (st != LBM_OK) return st;
   return plan_impl(c, num_q_tokens, 0, hip_stream);
 }
@@ -573,7 +585,7 @@ lbm_status lbm_plan(lbm_cache* c, int32_t num_q_tokens, void* hip_stream) {
 lbm_status lbm_plan_transient(lbm_cache* c, int32_t num_q_tokens, int32_t num_own_tokens,
                               void* hip_stream) {
   clear_error();
-  lbm_status st = check_cache(c);
+  lbm_status st = check_live(c);
   if (st != LBM_OK) return st;
   if (num_own_tokens < 1 || num_own_tokens > c->cfg.max_q_tokens)
     return fail(LBM_ERR_INVALID_ARG, "num_own_tokens %d outside 1..%d", num_own_tokens,
@@ -593,7 +605,7 @@ int32_t lbm_plan_num_splits(const lbm_cache* c) {
 lbm_status lbm_run(lbm_cache* c, int32_t block_idx, const void* q, void* out,
                    int32_t num_q_tokens, void* hip_stream) {
   clear_error();
-  lbm_status st = check_cache(c);
+  lbm_status st = check_live(c);
   if (st != LBM_OK) return st;
   if (block_idx < 0 || block_idx >= c->cfg.num_blocks)
     return fail(LBM_ERR_INVALID_ARG, "block_idx %d outside 0..%d", block_idx, c->cfg.num_blocks - 1);
@@ -619,7 +631,7 @@ lbm_status lbm_run(lbm_cache* c, int32_t block_idx, const void* q, void* out,
 lbm_status lbm_run_transient(lbm_cache* c, int32_t block_idx, const void* q, const void* k,
                              const void* v, void* out, int32_t num_q_tokens, void* hip_stream) {
   clear_error();
-  lbm_status st = check_cache(c);
+  lbm_status st = check_live(c);
   if (st != LBM_OK) return st;
   if (block_idx < 0 || block_idx >= c->cfg.num_blocks)
     return fail(LBM_ERR_INVALID_ARG, "block_idx %d outside 0..%d", block_idx, c->cfg.num_blocks - 1);
@@ -653,7 +665,7 @@ lbm_status lbm_run_batch(lbm_cache* const* caches, int32_t n, int32_t block_idx,
   const lbm_cache* c0 = caches[0];
   for (int32_t i = 0; i < n; ++i) {
     lbm_cache* c = caches[i];
-    lbm_status st = check_cache(c);
+    lbm_status st = check_live(c);
     if (st != LBM_OK) return st;
     for (int32_t j = 0; j < i; ++j)   // each cache's split partials live in its own workspace
       if (caches[j] == c) return fail(LBM_ERR_INVALID_ARG, "cache %d appears twice", i);
@@ -909,11 +921,12 @@ lbm_status lbm_graph_launch(lbm_graph* g, void* hip_stream) {
     if (e != hipSuccess) return hip_fail(e, "graph staging wait");
     g->pending[i] = false;
   }
+  if (c->poisoned) return fail(LBM_ERR_BAD_STATE, "a failed step left the cache unusable; reset it");
   lbm_status st = c->bk.reserve(g->nf);
   if (st != LBM_OK) return st;
-  std::vector<int32_t> evicted;
-  st = c->bk.evict(&evicted);
-  if (st != LBM_OK) return st;
+  // the visible set after this step's eviction: the latest sliding_window
+  // live pages, which the reservation's pages already are (eviction runs
+  // only once the launch is enqueued)
   const PlanInfo p = c->bk.plan_info();
   const WriteMap& wm = c->bk.write_map();
   StepDesc d;
@@ -936,8 +949,21 @@ lbm_status lbm_graph_launch(lbm_graph* g, void* hip_stream) {
                 sizeof(int32_t) * sp.size());
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   hipError_t e = hipGraphLaunch(g->exec[i], s);
-  if (e == hipSuccess) e = hipEventRecord(g->done[i], s);
-  if (e != hipSuccess) return hip_fail(e, "graph launch");
+  if (e != hipSuccess) {
+    // nothing of the step was enqueued: undo a one-frame reservation (no
+    // evict has run since it); a multi-frame one cannot be undone, so the
+    // cache refuses further steps until lbm_cache_reset
+    if (g->nf != 1 || c->bk.rollback() != LBM_OK) c->poisoned = true;
+    return hip_fail(e, "graph launch");
+  }
+  std::vector<int32_t> evicted;
+  (void)c->bk.evict(&evicted);  // the step is enqueued: commit it
+  e = hipEventRecord(g->done[i], s);
+  if (e != hipSuccess) {
+    // the staging slot can no longer be guarded; the step itself is queued
+    c->poisoned = true;
+    return hip_fail(e, "graph launch event");
+  }
   g->pending[i] = true;
   g->next = i ^ 1;
   // the cache is left as after the call sequence append(all blocks), evict, plan

@@ -219,3 +219,24 @@ def test_choose_splits():
     assert cs(1375, 99054, 16, 256, 2, 16, 0, 256) == 8
     assert cs(1375, 99054, 16, 256, 2, 16, 0, 128) == 10
     assert cs(1375, 99054, 16, 256, 2, 16, 0, -1) == 8   # non-positive: the 256-row default
+
+
+@pytest.mark.parametrize("cid", [0, 2, 4])
+def test_plan_before_evict_equals_plan_after(cid):
+    """A step's visible table does not depend on whether the eviction that
+    commits it has run yet: the graph launch builds the step's tables right
+    after the reservation and evicts only once the launch is enqueued.  A
+    one-frame reservation rolled back before that eviction (a failed launch)
+    leaves the state exactly as before the step."""
+    cfg = workloads.get_config(cid)
+    core, _ = _pair(cfg)
+    for s, nf in enumerate(workloads.step_schedule(cfg)):
+        before = core.dump()
+        core.append(nf)
+        if nf == 1 and s % 3 == 0:
+            core.rollback()
+            assert core.dump() == before
+            core.append(nf)
+        planned = core.plan()
+        core.evict()
+        assert core.plan() == planned
