@@ -19,7 +19,8 @@
 //    K and V operand read from LDS feeds two MFMAs.  A wavefront whose rows
 //    all lie past the step's queries only loads its share of each tile and
 //    keeps the barriers, so the step's last query group proceeds in step with
-//    the groups that share its key range (and its tiles in L2);
+//    the groups that share its key range (and its tiles in L2); one whose
+//    second half lies past them computes its first half only;
 //  * 64-key tiles of K and V go from HBM straight into LDS (row-major, global
 //    loads with an LDS destination, no staging registers) through rings of
 //    four stages each, three tiles ahead of use; one barrier per tile;
@@ -32,11 +33,15 @@
 //  * per-step row table (one code per key position) gives each K/V row's
 //    address, so the loop does no page arithmetic;
 //  * online softmax in fp32 with exp2 and the scale folded into Q, against a
-//    running max that the score MFMAs subtract themselves (each chain starts
-//    with an MFMA over a bias column that holds -max; the max stays on the
-//    input type's grid, so the bias is exact) and that is refreshed (O
-//    rescaled, the block's scores recomputed from LDS) only when a weight
-//    would exceed 256; row sums by 16-bit dot products of the rounded weights;
+//    stale running max: 0 unless a row's first max falls outside a window
+//    around 0 (wide for bf16, narrow for fp16) and raised (O rescaled, the
+//    block's scores recomputed from LDS) only when a lane's weights of a key
+//    block would sum past a type-dependent limit.  The common path computes
+//    scores from 0 and takes their exponentials as they are: no subtraction
+//    and no bias work.  A wavefront with some max not 0 ("biased") takes a
+//    slower path on every tile that subtracts the max on the vector ALU and
+//    redoes key block 0.  Row sums by 16-bit dot products of the rounded
+//    weights;
 //  * each tile in two 32-key blocks, in the order K Q^T (block 0), K Q^T
 //    (block 1) beside block 0's exponentials, P V (block 0) beside block 1's
 //    exponentials, P V (block 1), with the order pinned, so that the vector
@@ -44,7 +49,7 @@
 //  * O^T += V^T P^T on the same MFMA with P taken from registers (no LDS trip),
 //    P rounded to the input type (round to nearest even); the V operand comes from the
 //    row-major tile through gfx950's LDS transpose reads;
-//  * 240-246 VGPRs and no scratch, two workgroups per CU; the steady-state
+//  * 221-223 VGPRs and no scratch, two workgroups per CU; the steady-state
 //    loop takes four steps per iteration, so LDS operand offsets are constants;
 //  * with several splits, each writes (O, m, l) partials that a separate merge
 //    kernel combines (a kernel boundary orders them: no fences, which on this
@@ -65,8 +70,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// The element type's MFMA (32x32x16, fp32 accumulate) and pair dot product
-// (fp32 accumulate).
+// The element type's MFMA (32x32x16, fp32 accumulate), pair dot product
+// (fp32 accumulate) and the range limits of the weights:
+//  kJump: the largest sum of a lane's 16 weights of one key block before the
+//    running max is raised (keeps every weight, and P in the input type,
+//    finite);
+//  [kZeroLo, kZeroHi]: the window of a row's first max (base-2 units) in
+//    which the running max stays 0.
 template <typename T> struct Elt;
 template <> struct Elt<__bf16> {
   typedef __bf16 v8 __attribute__((ext_vector_type(8)));
@@ -77,6 +87,8 @@ template <> struct Elt<__bf16> {
   static __device__ __forceinline__ float dot2(v2 a, v2 b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
   }
+  static constexpr float kJump = 0x1p64f;
+  static constexpr float kZeroLo = -32.f, kZeroHi = 32.f;
 };
 template <> struct Elt<_Float16> {
   typedef _Float16 v8 __attribute__((ext_vector_type(8)));
@@ -87,6 +99,9 @@ template <> struct Elt<_Float16> {
   static __device__ __forceinline__ float dot2(v2 a, v2 b, float c) {
     return __builtin_amdgcn_fdot2(a, b, c, false);
   }
+  // fp16 tops out at 65504: weights stay below 2^12
+  static constexpr float kJump = 0x1p12f;
+  static constexpr float kZeroLo = -4.f, kZeroHi = 8.f;
 };
 
 constexpr int D = 64;
@@ -350,6 +365,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   };
   auto end_step = [&](int32_t i) __attribute__((always_inline)) {
     LBM_WAIT_VMCNT_LDS0(kInFlight);
+    asm volatile("" ::: "memory");  // the code reads below stay after the wait
     code_nx = codes_of(i + 1 + kLead);
     barrier();
   };
@@ -375,49 +391,57 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[h][db][e] = 0.f;
-  // per half: running max of the row's scores in base-2 units (stale between
-  // jumps) and this lane's share of the row sum relative to it
+  // per half: running max of the row's scores in base-2 units (0 until the
+  // row needs another, stale between jumps) and this lane's share of the row
+  // sum relative to it
   float m_run[2] = {0.f, 0.f};
   float l_run[2] = {0.f, 0.f};
+  // some half's running max is not 0 (wavefront-uniform): every tile then
+  // takes the rare path, which subtracts it from the scores
+  int32_t biased = 0;
   const h2 ones = {static_cast<T>(1.0f), static_cast<T>(1.0f)};
+  const f32x16 zero = {};
 
   // S^T[key][row] - m of key block kb (keys 32kb .. 32kb+31) of a tile, for
-  // both halves, in base-2 units: lane holds row l32 (+32h) and keys
-  // 32kb + 8j + 4hh + u (element 4j + u of s[h][kb]); each K operand read
-  // feeds both halves' MFMAs.  The chain starts with one more MFMA over a
-  // bias column: the key side holds 1 and the query side -m_run at
-  // contraction index 0 (lanes 0..31 hold indices 0..7 of both operands), so
-  // the accumulators start from -m_run without a move per element; m_run stays
-  // on T's grid, so the bias is exact.
-  h8 abias = {};
-  if (hh == 0) abias[0] = static_cast<T>(1.0f);
-  h8 bbias[2];
-  auto set_bias = [&](int h) __attribute__((always_inline)) {
-    bbias[h] = h8{};
-    if (hh == 0) bbias[h][0] = static_cast<T>(-m_run[h]);
-  };
-  set_bias(0);
-  set_bias(1);
-  auto start_block = [&](int kb, f32x16 (*s)[2]) __attribute__((always_inline)) {
+  // the wavefront's NH halves, in base-2 units: lane holds row l32 (+32h) and
+  // keys 32kb + 8j + 4hh + u (element 4j + u of s[h][kb]); each K operand
+  // read feeds every half's MFMA.  Each chain starts from 0; a biased
+  // wavefront then subtracts m_run on the vector ALU.
+  auto unbias = [&](auto b_c, auto nh_c, int kb, f32x16 (*s)[2]) __attribute__((always_inline)) {
+    if constexpr (decltype(b_c)::value) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) s[h][kb] = Elt<T>::mfma(abias, bbias[h], f32x16{});
+      for (int h = 0; h < decltype(nh_c)::value; ++h)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[h][kb][e] -= m_run[h];
+    }
   };
-  auto qk_block = [&](const uint16_t* K, int kb, f32x16 (*s)[2]) __attribute__((always_inline)) {
-    start_block(kb, s);
+  auto qk_block = [&](auto b_c, auto nh_c, const uint16_t* K, int kb, f32x16 (*s)[2])
+                      __attribute__((always_inline)) {
+    constexpr int NH = decltype(nh_c)::value;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const h8 kf = *reinterpret_cast<const h8*>(K + k_row + kb * 32 * LS +
                                                  (((2 * ks + hh) ^ k_x) * 8));
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        s[h][kb] = Elt<T>::mfma(kf, qf[h][ks], s[h][kb]);
+      for (int h = 0; h < NH; ++h)
+        s[h][kb] = Elt<T>::mfma(kf, qf[h][ks], ks == 0 ? zero : s[h][kb]);
     }
+    unbias(b_c, nh_c, kb, s);
+  };
+  // the same with the bias taken at run time (the rare paths)
+  auto qk_block_any = [&](auto nh_c, const uint16_t* K, int kb, f32x16 (*s)[2])
+                          __attribute__((always_inline)) {
+    if (__builtin_amdgcn_readfirstlane(biased))
+      qk_block(std::true_type{}, nh_c, K, kb, s);
+    else
+      qk_block(std::false_type{}, nh_c, K, kb, s);
   };
   // on the split's last tile, keys of block kb past the visible set
-  auto mask_block = [&](int32_t i, int kb, f32x16 (*s)[2]) __attribute__((always_inline)) {
+  auto mask_block = [&](auto nh_c, int32_t i, int kb, f32x16 (*s)[2]) __attribute__((always_inline)) {
+    constexpr int NH = decltype(nh_c)::value;
     const int32_t lim = a.kv_len - (t_begin + i) * 64 - 4 * hh;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         s[h][kb][e] = kb * 32 + 8 * (e >> 2) + (e & 3) >= lim ? -INFINITY : s[h][kb][e];
@@ -426,10 +450,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   // PV MFMA (group G = 2kb + g holds elements 8g..8g+7 of s[h][kb]); lt[h]
   // receives this lane's sum of the rounded p (exactly the weights the PV
   // product uses)
-  auto exp_block = [&](const f32x16 (*s)[2], int kb, const float* shift, h8 (*pb)[4], float* lt)
-                       __attribute__((always_inline)) {
+  auto exp_block = [&](auto nh_c, const f32x16 (*s)[2], int kb, const float* shift, h8 (*pb)[4],
+                       float* lt) __attribute__((always_inline)) {
+    constexpr int NH = decltype(nh_c)::value;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NH; ++h) {
       lt[h] = 0.f;
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
@@ -459,8 +484,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     }
   };
   // O^T[d][row] += V^T[d][keys] P^T[keys][row] over key block kb; each V
-  // operand read feeds both halves' MFMAs
-  auto pv_block = [&](const uint16_t* V, int kb, const h8 (*pb)[4]) __attribute__((always_inline)) {
+  // operand read feeds every half's MFMA
+  auto pv_block = [&](auto nh_c, const uint16_t* V, int kb, const h8 (*pb)[4]) __attribute__((always_inline)) {
+    constexpr int NH = decltype(nh_c)::value;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -468,7 +494,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
         const uint16_t* p = V + (db == 0 ? v_rd0 : v_rd1) + (16 * G) * LS;
         const h8 vf = v_operand<h8>(p, p + 8 * LS);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) o[h][db] = Elt<T>::mfma(vf, pb[h][G], o[h][db]);
+        for (int h = 0; h < NH; ++h) o[h][db] = Elt<T>::mfma(vf, pb[h][G], o[h][db]);
       }
   };
   // the row's max over key blocks kb0 .. kb1 minus m_run (both lanes of the
@@ -493,113 +519,141 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[h][db][e] *= alpha;
     m_run[h] = m_new;
-    set_bias(h);
   };
-  // One tile: scores, weights, and O += P V for both halves, by key block so
-  // that each block's exponentials run beside the other block's MFMAs: K Q^T
-  // of block 0; K Q^T of block 1 beside block 0's weights; P V of block 0
-  // beside block 1's weights; P V of block 1.  Softmax runs against the
-  // running max as it stands (the scores arrive with it subtracted).  On the
-  // split's first tile the max is the tile's own, so the largest weight is 1
-  // and the row sum never underflows; afterwards the max is raised only when
-  // some lane's weights of a block would sum past 256 (a jump of the max):
-  // then the block's scores are recomputed from the stage (resident until the
-  // step's barrier), O and l rescaled and the block's weights redone (a jump
-  // in block 0 also shifts block 1's scores; one in block 1 finds block 0's
-  // terms already in O, which the rescale carries to the new max).  Any max
-  // not below the true one gives the same quotient, since numerator and
-  // denominator share it.
-  auto tile = [&](int32_t i, bool first, bool last, int stage) __attribute__((always_inline)) {
+  // One tile: scores, weights, and O += P V for the wavefront's NH halves,
+  // by key block so that each block's exponentials run beside the other
+  // block's MFMAs: K Q^T of block 0; K Q^T of block 1 beside block 0's
+  // weights; P V of block 0 beside block 1's weights; P V of block 1.
+  // Softmax runs against the running max as it stands (the scores arrive
+  // with it subtracted).  On the split's first tile a row whose max lies
+  // outside [kZeroLo, kZeroHi] takes that max (so the largest weight is 1
+  // and the row sum never underflows); others keep 0.  Afterwards the max is
+  // raised only when some lane's weights of a block would sum past kJump (a
+  // jump of the max): then the block's scores are recomputed from the stage
+  // (resident until the step's barrier), O and l rescaled and the block's
+  // weights redone (a jump in block 0 also shifts block 1's scores; one in
+  // block 1 finds block 0's terms already in O, which the rescale carries to
+  // the new max).  Any max not below the true one gives the same quotient,
+  // since numerator and denominator share it.
+  auto tile = [&](auto nh_c, int32_t i, bool first, bool last, int stage)
+                  __attribute__((always_inline)) {
+    constexpr int NH = decltype(nh_c)::value;
     const uint16_t* K = lds_k[stage];
     const uint16_t* V = lds_v[stage];
     f32x16 s[2][2];
     h8 pb[2][4];
     float lt0[2], lt1[2];
-    qk_block(K, 0, s);
-    if (last) mask_block(i, 0, s);
+    // scores against a running max of 0 (the rare path below corrects a
+    // biased wavefront's)
+    qk_block(std::false_type{}, nh_c, K, 0, s);
+    if (last) mask_block(nh_c, i, 0, s);
     if (first) {
-      qk_block(K, 1, s);
-      if (last) mask_block(i, 1, s);
+      // the split's first tile (the running max is 0 here)
+      qk_block(std::false_type{}, nh_c, K, 1, s);
+      if (last) mask_block(nh_c, i, 1, s);
+      float r[2];
+      bool out[2];
+      bool any = false;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        m_run[h] = round_up_to<T>(row_max(s[h], 0, 1));
-        set_bias(h);
+      for (int h = 0; h < NH; ++h) {
+        r[h] = row_max(s[h], 0, 1);
+        out[h] = !(r[h] >= Elt<T>::kZeroLo && r[h] <= Elt<T>::kZeroHi);
+        any = any || out[h];
       }
-      exp_block(s, 0, m_run, pb, lt0);
-      exp_block(s, 1, m_run, pb, lt1);
-    } else {
-      // block 1's K Q^T MFMAs, each followed by four of block 0's weights
-      // (the fences pin the order, so the vector ALU works while the matrix
-      // cores do)
-      h8 kf1[4];
+      if (__ballot(any)) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        kf1[ks] = *reinterpret_cast<const h8*>(K + k_row + 32 * LS + (((2 * ks + hh) ^ k_x) * 8));
-      lt0[0] = lt0[1] = 0.f;
-      start_block(1, s);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const int ks = st >> 1, h = st & 1;
-        s[h][1] = Elt<T>::mfma(kf1[ks], qf[h][ks], s[h][1]);
-        exp_part(s, st >> 2, 0, st & 3, pb, lt0);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int h = 0; h < NH; ++h) m_run[h] = out[h] ? round_up_to<T>(r[h]) : 0.f;
+        biased = 1;
       }
-      if (last) mask_block(i, 1, s);
-      if (__ballot(!(lt0[0] <= 256.f) || !(lt0[1] <= 256.f))) {
-        qk_block(K, 0, s);
-        if (last) mask_block(i, 0, s);
-        float su[2];
+      exp_block(nh_c, s, 0, m_run, pb, lt0);
+      exp_block(nh_c, s, 1, m_run, pb, lt1);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          su[h] = fmaxf(row_max(s[h], 0, 0), 0.f);
-          raise_max(h, su[h]);
-#pragma unroll
-          for (int e = 0; e < 16; ++e) s[h][1][e] -= su[h];
-        }
-        exp_block(s, 0, su, pb, lt0);
-      }
-      l_run[0] += lt0[0];
-      l_run[1] += lt0[1];
-      // block 0's P V MFMAs, each after four of block 1's weights
-      h8 vf0[4];
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int G = 0; G < 2; ++G) {
-          const uint16_t* p = V + (db == 0 ? v_rd0 : v_rd1) + (16 * G) * LS;
-          vf0[2 * db + G] = v_operand<h8>(p, p + 8 * LS);
-        }
-      lt1[0] = lt1[1] = 0.f;
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const int db = st >> 2, G = (st >> 1) & 1, h = st & 1;
-        exp_part(s, st >> 2, 1, st & 3, pb, lt1);
-        o[h][db] = Elt<T>::mfma(vf0[2 * db + G], pb[h][G], o[h][db]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (__ballot(!(lt1[0] <= 256.f) || !(lt1[1] <= 256.f))) {
-        qk_block(K, 1, s);
-        if (last) mask_block(i, 1, s);
-        float su[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          su[h] = fmaxf(row_max(s[h], 1, 1), 0.f);
-          raise_max(h, su[h]);
-        }
-        exp_block(s, 1, su, pb, lt1);
-      }
-      l_run[0] += lt1[0];
-      l_run[1] += lt1[1];
-      pv_block(V, 1, pb);
+      for (int h = 0; h < NH; ++h) l_run[h] += lt0[h] + lt1[h];
+      pv_block(nh_c, V, 0, pb);
+      pv_block(nh_c, V, 1, pb);
       return;
     }
+    // block 1's K Q^T MFMAs, each followed by four of block 0's weights
+    // (the fences pin the order, so the vector ALU works while the matrix
+    // cores do)
+    h8 kf1[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) l_run[h] += lt0[h] + lt1[h];
-    pv_block(V, 0, pb);
-    pv_block(V, 1, pb);
+    for (int ks = 0; ks < 4; ++ks)
+      kf1[ks] = *reinterpret_cast<const h8*>(K + k_row + 32 * LS + (((2 * ks + hh) ^ k_x) * 8));
+    lt0[0] = lt0[1] = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < 4 * NH; ++st) {
+      const int ks = st / NH, h = st % NH;
+      s[h][1] = Elt<T>::mfma(kf1[ks], qf[h][ks], ks == 0 ? zero : s[h][1]);
+      exp_part(s, st >> 2, 0, st & 3, pb, lt0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (last) mask_block(nh_c, i, 1, s);
+    bool jump = false;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) jump = jump || !(lt0[h] <= Elt<T>::kJump);
+    const bool rare = __ballot(jump) != 0 || __builtin_amdgcn_readfirstlane(biased) != 0;
+    if (__builtin_expect(rare, 0)) {
+      // a jump in block 0, or a biased wavefront: both blocks' scores
+      // against the running max, then block 0's weights redone against the
+      // raised one
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[h][1][e] -= m_run[h];
+      qk_block_any(nh_c, K, 0, s);
+      if (last) mask_block(nh_c, i, 0, s);
+      float su[2];
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        su[h] = fmaxf(row_max(s[h], 0, 0), 0.f);
+        raise_max(h, su[h]);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[h][1][e] -= su[h];
+      }
+      biased = 1;
+      exp_block(nh_c, s, 0, su, pb, lt0);
+    }
+#pragma unroll
+    for (int h = 0; h < NH; ++h) l_run[h] += lt0[h];
+    // block 0's P V MFMAs, each after four of block 1's weights
+    h8 vf0[4];
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int G = 0; G < 2; ++G) {
+        const uint16_t* p = V + (db == 0 ? v_rd0 : v_rd1) + (16 * G) * LS;
+        vf0[2 * db + G] = v_operand<h8>(p, p + 8 * LS);
+      }
+    lt1[0] = lt1[1] = 0.f;
+#pragma unroll
+    for (int st = 0; st < 4 * NH; ++st) {
+      const int mi = st / NH, h = st % NH;
+      const int db = mi >> 1, G = mi & 1;
+      exp_part(s, st >> 2, 1, st & 3, pb, lt1);
+      o[h][db] = Elt<T>::mfma(vf0[2 * db + G], pb[h][G], o[h][db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    jump = false;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) jump = jump || !(lt1[h] <= Elt<T>::kJump);
+    if (__ballot(jump)) {
+      qk_block_any(nh_c, K, 1, s);
+      if (last) mask_block(nh_c, i, 1, s);
+      float su[2];
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        su[h] = fmaxf(row_max(s[h], 1, 1), 0.f);
+        raise_max(h, su[h]);
+      }
+      biased = 1;
+      exp_block(nh_c, s, 1, su, pb, lt1);
+    }
+#pragma unroll
+    for (int h = 0; h < NH; ++h) l_run[h] += lt1[h];
+    pv_block(nh_c, V, 1, pb);
   };
-
   // Prologue: row codes of positions 0 .. 2kLead-1, then K and V of
   // positions 0 .. kLead-1; position 0 resident before the first step.
 #pragma unroll
@@ -622,11 +676,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     LBM_WAIT_VMCNT(0);
     return;
   }
-  if (n_t == 1) {
-    tile(0, true, true, 0);
-  } else {
+  // NH halves hold rows: a wavefront whose second half lies past the step's
+  // queries (in the last query group) runs the first half only
+  auto steps = [&](auto nh_c) __attribute__((always_inline)) {
+    if (n_t == 1) {
+      tile(nh_c, 0, true, true, 0);
+      return;
+    }
     step_loads(0);
-    tile(0, true, false, 0);
+    tile(nh_c, 0, true, false, 0);
     end_step(0);
     // four steps per iteration, so that each tile's stage (i mod 4, with i = 1
     // mod 4 at the top) is a constant and its LDS operand addresses fold into
@@ -634,25 +692,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     int32_t i = 1;
     for (; i + 4 < n_t; i += 4) {
       step_loads(i);
-      tile(i, false, false, 1);
+      tile(nh_c, i, false, false, 1);
       end_step(i);
       step_loads(i + 1);
-      tile(i + 1, false, false, 2);
+      tile(nh_c, i + 1, false, false, 2);
       end_step(i + 1);
       step_loads(i + 2);
-      tile(i + 2, false, false, 3);
+      tile(nh_c, i + 2, false, false, 3);
       end_step(i + 2);
       step_loads(i + 3);
-      tile(i + 3, false, false, 0);
+      tile(nh_c, i + 3, false, false, 0);
       end_step(i + 3);
     }
     for (; i + 1 < n_t; ++i) {
       step_loads(i);
-      tile(i, false, false, i & (NST - 1));
+      tile(nh_c, i, false, false, i & (NST - 1));
       end_step(i);
     }
-    tile(n_t - 1, false, true, (n_t - 1) & (NST - 1));
-  }
+    tile(nh_c, n_t - 1, false, true, (n_t - 1) & (NST - 1));
+  };
+  if (w_row0 + 32 >= a.Tq)
+    steps(std::integral_constant<int, 1>{});
+  else
+    steps(std::integral_constant<int, 2>{});
 
   // loads of clamped positions may still be in flight: the workgroup's LDS
   // must not be released under them

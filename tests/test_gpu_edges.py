@@ -159,14 +159,18 @@ def test_running_max_jumps(dtype, head_dim, splits):
     # planted row j (query row 3j) jumps at JUMPS[j % 6] shifted by 2(j // 6),
     # and, for even j, again at JUMPS[(j + 2) % 6] shifted by 2(j // 6) + 1
     # with a larger score (no two plants share a key): K at that key is a
-    # multiple of the row's query for head j % H, placing its score ~20 (first)
-    # or ~43 (second) log2 units above the unplanted ones
+    # multiple of the row's query for head j % H, placing its score s1
+    # (first) or s2 (second) above the unplanted ones.  The 16-bit kernel
+    # lets weights grow to 2^64 (bf16) or 2^12 (fp16) past a running max of
+    # 0 before it raises the max, so the bf16 plants sit ~72 and ~144 log2
+    # units up (each past the limit), the others ~20 and ~43.
+    s1, s2 = (50.0, 100.0) if dtype == "bf16" else (14.0, 30.0)
     for j, r in enumerate(range(0, tq, 3)):
         h = j % H
         qr = q[r, h].float()
-        plants = [(JUMPS[j % 6], 2 * (j // 6), 14.0)]
+        plants = [(JUMPS[j % 6], 2 * (j // 6), s1)]
         if j % 2 == 0:
-            plants.append((JUMPS[(j + 2) % 6], 2 * (j // 6) + 1, 30.0))
+            plants.append((JUMPS[(j + 2) % 6], 2 * (j // 6) + 1, s2))
         for (t, k), off, score in plants:
             pos = t * 64 + k + off
             assert pos < kv
@@ -186,7 +190,7 @@ def test_running_max_jumps(dtype, head_dim, splits):
                             pid_d.data_ptr(), n_pp, sid_d.data_ptr(), n_st, ws.data_ptr(),
                             torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    # the planted keys dominate their rows (a weight of 2^14 or more against
+    # the planted keys dominate their rows (a weight of 2^8 or more against
     # the rest), which the test checks so that it exercises what it claims
     s = np.einsum("qhd,khd->qhk", q_h, K) / np.sqrt(D) * np.log2(np.e)
     lead = [s[r, j % H].max() - np.partition(s[r, j % H], -2)[-2]
@@ -194,3 +198,55 @@ def test_running_max_jumps(dtype, head_dim, splits):
     assert min(lead) > 8.0, f"planted jumps too small: {min(lead):.1f}"
     st = compare(out.double().cpu().numpy(), ref, dtype, f"{dtype} jumps splits={splits}")
     say(f"{dtype} splits={splits}: max-abs {st['max_abs']:.3e}, smallest lead {min(lead):.1f}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_rows_far_from_zero(dtype, splits):
+    """Rows whose every score lies far above or far below 0 (log2 units),
+    beside ordinary rows in the same wavefronts: the 16-bit kernel keeps a
+    row's running max at 0 while its first scores stay in a window around 0,
+    and otherwise starts it at their max and subtracts it from every later
+    score (the biased path).  Head 1's keys get a constant added to feature
+    0, and some query rows a large +-value there, which shifts each of those
+    rows' scores by about +-90 log2 units; compared with dense attention (the
+    oracle) over the same rows.  (The fp32 kernel has no such path; its
+    tolerance, set for scores of ordinary size, does not cover scores this
+    large, whose fp32 rounding grows with their magnitude.)"""
+    D = 64
+    n_pp, n_st = 7, 91                    # 791 keys: 12 full tiles and a 23-key tail
+    kv = n_pp * P + n_st
+    seed0 = 9600 + 10 * DTYPE_CODE[dtype] + splits
+    pp = workloads.gen_normal((N_PP, 2, P, H, D), seed0 + 1, dtype, DEV)
+    sp = workloads.gen_normal((N_SP, 2, SPS, H, D), seed0 + 2, dtype, DEV)
+    tq = 200
+    q = workloads.gen_normal((tq, H, D), seed0 + 3, dtype, DEV)
+    pp[:, 0, :, 1, 0] += 8.0
+    sp[:, 0, :, 1, 0] += 8.0
+    # rows 4i get +64 in feature 0 of head 1, rows 4i+1 get -64: 8 * 64 / 8 =
+    # 64 natural units (~92 log2 units) of shift, plus a spread of ~12 log2
+    # units per key from the keys' own feature 0
+    q[0::4, 1, 0] = 64.0
+    q[1::4, 1, 0] = -64.0
+    rng = np.random.default_rng(seed0)
+    pid = rng.permutation(N_PP).astype(np.int32)
+    sid = rng.permutation(N_SP).astype(np.int32)
+    pp_h, sp_h, q_h = pp.double().cpu().numpy(), sp.double().cpu().numpy(), q.double().cpu().numpy()
+    K = np.concatenate([pp_h[p, 0] for p in pid[:n_pp]] + [sp_h[s, 0] for s in sid])[:kv]
+    V = np.concatenate([pp_h[p, 1] for p in pid[:n_pp]] + [sp_h[s, 1] for s in sid])[:kv]
+    ref = dense_attention(q_h, K, V)
+    # the shifted rows' scores really lie outside the window (all above 32 or
+    # all below -32 log2 units)
+    s = np.einsum("qd,kd->qk", q_h[:, 1], K[:, 1]) / np.sqrt(D) * np.log2(np.e)
+    assert s[0::4].min() > 32.0 and s[1::4].max() < -32.0, (s[0::4].min(), s[1::4].max())
+    cfg = _config(dtype, D, splits)
+    ws = torch.empty(lbm.lbm_query_sizes(cfg)[2], dtype=torch.uint8, device=DEV)
+    out = torch.full_like(q, float("nan"))
+    pid_d = torch.from_numpy(pid).to(DEV)   # kept alive until the launch has run
+    sid_d = torch.from_numpy(sid).to(DEV)
+    lbm.lbm_paged_attention(cfg, q.data_ptr(), out.data_ptr(), tq, pp.data_ptr(), sp.data_ptr(),
+                            pid_d.data_ptr(), n_pp, sid_d.data_ptr(), n_st, ws.data_ptr(),
+                            torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    st = compare(out.double().cpu().numpy(), ref, dtype, f"{dtype} far rows splits={splits}")
+    say(f"{dtype} splits={splits}: max-abs {st['max_abs']:.3e}")
