@@ -6,14 +6,20 @@ attention (HIP, bf16 MFMA).  Shapes: 1369 patch + 6 special tokens per frame,
 16 heads x 64, scale_frames 8, sliding_window 64, bf16 unit-normal inputs.
 
 Setup (untimed): the 8-frame first step and 64 single frames (F = 72, the
-window full), then W warm-up steps; then K timed steps.  The defaults stream
-the full 1000 frames (F = 81..1000 timed).  Inputs: 8 distinct seeded input
-sets per block, drawn up front and resident in HBM, cycled over the steps.
+window full), then W warm-up steps; then K timed steps (the first window,
+which gives value and roofline).  Inputs: 8 distinct seeded input sets per
+block, drawn up front and resident in HBM, cycled over the steps.
+
+The work per frame grows by 6 special keys a frame, so two more windows are
+timed ('windows' in the line): the last 20 frames of the 1000-frame stream
+(F = 981..1000), reached after the first window by appends and evictions
+only, and the last 20 frames of the 10,000-frame 4-block stream (F =
+9981..10000, 38% of the keys special), reached the same way.
 
 Printed: one JSON line with frames/s (value), the attention kernel's roofline
 (algorithmic FLOPs per launch / launch time from HIP events on the launch
-stream, against the bf16 dense MFMA peak) and the CPU oracle timed on a
-bounded sample of the same step.
+stream, against the bf16 dense MFMA peak), the windows, and the CPU oracle
+timed on a bounded sample of the same step.
 """
 from __future__ import annotations
 
@@ -37,7 +43,7 @@ N_INPUT_SETS = 8
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=920)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -47,6 +53,14 @@ def parse():
                     help="timed steps of the fp16 and the no-scale-frames variants of the workload "
                          "(reported under 'variants')")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--end-steps", type=int, default=20,
+                    help="timed frames at the end of the 1000-frame stream, reached after the "
+                         "timed window by appends and evictions only (reported under 'windows')")
+    ap.add_argument("--long-end-steps", type=int, default=20,
+                    help="timed frames at the end of the 10,000-frame 4-block stream (reported "
+                         "under 'windows')")
+    ap.add_argument("--no-windows", action="store_true",
+                    help="time the first window only (no end-of-stream windows)")
     ap.add_argument("--f32-steps", type=int, default=20,
                     help="timed steps of the fp32 (force_fp32) variant (reported under 'variants')")
     ap.add_argument("--graph-steps", type=int, default=100,
@@ -188,96 +202,159 @@ def pmc_summary(fetch_dir, write_dir):
         fh.write("HBM traffic of one lbm_run (attention + merge) and of one single-frame "
                  "append, 24-block ViT-L step; written by "
                  "'bench.py --pmc-summary' from two rocprofv3 --pmc runs of 'bench.py --steps 2 "
-                 "--warmup 0 --no-cpu-baseline --no-variants --calibrate-copy' (FETCH_SIZE, "
+                 "--warmup 0 --no-cpu-baseline --no-variants --no-windows --calibrate-copy' (FETCH_SIZE, "
                  "then WRITE_SIZE)\n")
         fh.write(json.dumps(rec, indent=1) + "\n")
     print(json.dumps(rec))
 
 
 
-def measure_stream(cfg, dev, steps, warmup, splits_req=0, keep=False, skip_steps=0):
-    """Stream ``cfg`` through its first step and the window fill, ``warmup``
-    more steps, then time ``steps`` frame steps (all blocks: append, evict and
-    plan once, attention), with HIP events around one lbm_run per step (block
-    i mod B of step i: every block's launch has the same shape within a step,
-    and an event pair at every launch would itself add ~6 us of queue work per
-    event to the steps being timed) and one pair around the appends of blocks
-    1 .. B-1 of one further step; then ``skip_steps`` skip-append frames (each
-    frame's queries over the visible set and its own rows, nothing stored).
-    Returns the figures (and, with ``keep``, the live cache and inputs for the
-    CPU baseline)."""
-    import torch
+class Stream:
+    """One synthetic stream of ``cfg`` in a live cache: the first step, then
+    single frames drawn from N_INPUT_SETS seeded input sets per block (resident
+    in HBM, cycled).  A frame step appends every block's rows, evicts and
+    plans once (at block 0) and runs attention per block; a fast-forward step
+    (``run=False``) appends and evicts only."""
 
-    import paged_kv_cache_312_amd as lbm
-    import workloads
+    def __init__(self, cfg, dev, splits_req=0):
+        import torch
 
-    B, H, D, T = cfg.num_blocks, cfg.num_heads, cfg.head_dim, cfg.tokens_per_frame
-    fields = workloads.lbm_config_fields(cfg, num_splits=splits_req)
-    cache = lbm.PagedKVCache(lbm.make_config(**fields), dev)
-    stream = torch.cuda.current_stream()
+        import paged_kv_cache_312_amd as lbm
+        import workloads
 
-    # inputs: the first step, then N_INPUT_SETS single-frame sets per block
-    init = [workloads.gen_step_qkv(cfg, b, 0, cfg.initial_frames, dev) for b in range(B)]
-    sets = [[workloads.gen_step_qkv(cfg, b, 1 + i, 1, dev) for b in range(B)]
-            for i in range(N_INPUT_SETS)]
-    outs = [torch.empty((T, H, D), dtype=cache.dtype, device=dev) for _ in range(B)]
-    out_init = torch.empty((cfg.initial_frames * T, H, D), dtype=cache.dtype, device=dev)
-    torch.cuda.synchronize()
+        self.cfg, self.dev = cfg, dev
+        B, H, D, T = cfg.num_blocks, cfg.num_heads, cfg.head_dim, cfg.tokens_per_frame
+        fields = workloads.lbm_config_fields(cfg, num_splits=splits_req)
+        self.cache = lbm.PagedKVCache(lbm.make_config(**fields), dev)
+        self.stream = torch.cuda.current_stream()
+        self.init = [workloads.gen_step_qkv(cfg, b, 0, cfg.initial_frames, dev) for b in range(B)]
+        self.sets = [[workloads.gen_step_qkv(cfg, b, 1 + i, 1, dev) for b in range(B)]
+                     for i in range(N_INPUT_SETS)]
+        self.outs = [torch.empty((T, H, D), dtype=self.cache.dtype, device=dev) for _ in range(B)]
+        self.F = 0
+        self.step_idx = 0
+        torch.cuda.synchronize()
 
-    def frame_step(inputs, out_bufs, nq, ev=None, ev_block=-1):
-        for b in range(B):
+    def frame_step(self, inputs, out_bufs, nq, ev=None, ev_block=-1, run=True):
+        cache = self.cache
+        for b in range(self.cfg.num_blocks):
             q, k, v = inputs[b]
             cache.append_frame(b, k, v)
             if b == 0:
                 cache.evict_frames()
-                cache.plan(nq)
+                if run:
+                    cache.plan(nq)
+            if not run:
+                continue
             if b == ev_block:
-                ev[0].record(stream)
+                ev[0].record(self.stream)
             cache.run(b, q, out_bufs[b])
             if b == ev_block:
-                ev[1].record(stream)
+                ev[1].record(self.stream)
 
-    frame_step(init, [out_init] * B, cfg.initial_frames * T)
-    F = cfg.initial_frames
-    step_idx = 0
-    while F < cfg.scale_frames + cfg.sliding_window:
-        frame_step(sets[step_idx % N_INPUT_SETS], outs, T)
-        F += 1
-        step_idx += 1
-    for _ in range(warmup):
-        frame_step(sets[step_idx % N_INPUT_SETS], outs, T)
-        F += 1
-        step_idx += 1
-    torch.cuda.synchronize()
-    F_first = F + 1
+    def first(self, run=True):
+        """The first step (initial_frames frames)."""
+        import torch
+        cfg = self.cfg
+        out_init = None
+        if run:
+            out_init = torch.empty((cfg.initial_frames * cfg.tokens_per_frame, cfg.num_heads,
+                                    cfg.head_dim), dtype=self.cache.dtype, device=self.dev)
+        self.frame_step(self.init, [out_init] * cfg.num_blocks,
+                        cfg.initial_frames * cfg.tokens_per_frame, run=run)
+        self.F = cfg.initial_frames
 
-    # timed region: K steps; one attention launch per step bracketed by events
-    # on the launch stream for the roofline figure
-    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-          for _ in range(steps)]
-    kv_lens = []
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        frame_step(sets[step_idx % N_INPUT_SETS], outs, T, ev[i], i % B)
-        F += 1
-        step_idx += 1
-        kv_lens.append(cache.get_plan()[0] if i == 0 else kv_lens[-1] + cfg.special_per_frame)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    splits = cache.num_splits()
-    assert cache.stats()["frame_count"] == F
+    def advance(self, n, run=True):
+        """n single-frame steps (with attention, or appends and evictions only)."""
+        T = self.cfg.tokens_per_frame
+        for _ in range(n):
+            self.frame_step(self.sets[self.step_idx % N_INPUT_SETS], self.outs, T, run=run)
+            self.F += 1
+            self.step_idx += 1
 
-    attn_ms = 0.0
-    flops = 0.0          # algorithmic FLOPs of the bracketed launches
-    for i in range(steps):
-        attn_ms += ev[i][0].elapsed_time(ev[i][1])
-        flops += 4.0 * T * kv_lens[i] * H * D
-    n_launch = steps
-    avg_launch_ms = attn_ms / n_launch
-    achieved_tflops = flops / (attn_ms * 1e-3) / 1e12
-    ms_per_step = elapsed * 1e3 / steps
-    fps = steps / elapsed
+    def window(self, steps):
+        """Time ``steps`` frame steps: wall clock over the whole steps, and HIP
+        events on the launch stream around one lbm_run per step (block i mod B
+        of step i: every block's launch has the same shape within a step, and
+        an event pair at every launch would itself add ~6 us of queue work per
+        event to the steps being timed)."""
+        import statistics
+
+        import torch
+        cfg = self.cfg
+        B, H, D, T = cfg.num_blocks, cfg.num_heads, cfg.head_dim, cfg.tokens_per_frame
+        F_first = self.F + 1
+        ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+              for _ in range(steps)]
+        kv_lens = []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.frame_step(self.sets[self.step_idx % N_INPUT_SETS], self.outs, T, ev[i], i % B)
+            self.F += 1
+            self.step_idx += 1
+            # past the window fill every frame adds special_per_frame keys
+            kv_lens.append(self.cache.get_plan()[0] if i == 0
+                           else kv_lens[-1] + cfg.special_per_frame)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        assert self.cache.stats()["frame_count"] == self.F
+        launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+        flops = sum(4.0 * T * kv * H * D for kv in kv_lens)
+        attn_ms = sum(launch_ms)
+        return {"fps": steps / elapsed, "ms_per_step": elapsed * 1e3 / steps,
+                "tflops": flops / (attn_ms * 1e-3) / 1e12, "avg_launch_ms": attn_ms / steps,
+                "median_launch_ms": statistics.median(launch_ms), "flops": flops,
+                "n_launch": steps, "kv_lens": kv_lens, "splits": self.cache.num_splits(),
+                "F_first": F_first, "F_last": self.F}
+
+    def close(self):
+        self.cache.close()
+
+
+def window_record(w, peak, blocks):
+    """The JSON form of one timed window."""
+    return {"timed_frames": [w["F_first"], w["F_last"]], "kv_len": [w["kv_lens"][0], w["kv_lens"][-1]],
+            "blocks": blocks, "value": round(w["fps"], 3), "unit": "frames/s",
+            "ms_per_step": round(w["ms_per_step"], 4),
+            "attention_tflops": round(w["tflops"], 2), "frac": round(w["tflops"] / peak, 4),
+            "avg_launch_ms": round(w["avg_launch_ms"], 4),
+            "median_launch_ms": round(w["median_launch_ms"], 4), "key_splits": w["splits"]}
+
+
+def measure_end_window(cfg, dev, steps, splits_req=0):
+    """The last ``steps`` frames of ``cfg``'s stream: the frames before them
+    only append and evict (no attention), then the timed window."""
+    s = Stream(cfg, dev, splits_req)
+    try:
+        s.first(run=False)
+        s.advance(cfg.total_frames - steps - s.F, run=False)
+        return s.window(steps)
+    finally:
+        s.close()
+
+
+def measure_stream(cfg, dev, steps, warmup, splits_req=0, keep=False, skip_steps=0,
+                   end_steps=0):
+    """Stream ``cfg`` through its first step and the window fill, ``warmup``
+    more steps, then time ``steps`` frame steps (all blocks: append, evict and
+    plan once, attention) and one event pair around the appends of blocks
+    1 .. B-1 of one further step; then, with ``end_steps``, append and evict
+    only up to the stream's last ``end_steps`` frames and time those; then
+    ``skip_steps`` skip-append frames (each frame's queries over the visible
+    set and its own rows, nothing stored).  Returns the figures (and, with
+    ``keep``, the live cache and inputs for the CPU baseline)."""
+    import torch
+
+    B, H, D, T = cfg.num_blocks, cfg.num_heads, cfg.head_dim, cfg.tokens_per_frame
+    st = Stream(cfg, dev, splits_req)
+    cache, stream, sets, outs = st.cache, st.stream, st.sets, st.outs
+    st.first()
+    st.advance(cfg.scale_frames + cfg.sliding_window - st.F)
+    st.advance(warmup)
+    torch.cuda.synchronize()
+    w = st.window(steps)
+    F, step_idx = st.F, st.step_idx
 
     # append bandwidth: one more full step whose appends of blocks 1 .. B-1 go
     # back to back between one event pair.  Block 0's append (which reserves
@@ -298,19 +375,28 @@ def measure_stream(cfg, dev, steps, warmup, splits_req=0, keep=False, skip_steps
     for b in range(1, B):
         cache.run(b, inputs[b][0], outs[b])
     torch.cuda.synchronize()
+    st.F += 1
+    st.step_idx += 1
     app_ms = e_app[0].elapsed_time(e_app[1]) / (B - 1)
     app_bytes = 2 * 2 * T * H * D * cache.dtype.itemsize  # K and V rows, read + write
     append_gbps = app_bytes / (app_ms * 1e-3) / 1e9
 
+    # the stream's last end_steps frames, reached by appends and evictions only
+    end = None
+    if end_steps > 0 and st.F + end_steps <= cfg.total_frames:
+        st.advance(cfg.total_frames - end_steps - st.F, run=False)
+        end = st.window(end_steps)
+
     skip = None
     if skip_steps > 0:
         kv_cache = cache.get_plan()[0]
+        F_skip = st.F
         ev_s = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
                 for _ in range(skip_steps)]
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         for i in range(skip_steps):
-            inputs = sets[(step_idx + 1 + i) % N_INPUT_SETS]
+            inputs = sets[(st.step_idx + i) % N_INPUT_SETS]
             cache.plan_transient(T, T)
             for b in range(B):
                 q, k, v = inputs[b]
@@ -324,18 +410,21 @@ def measure_stream(cfg, dev, steps, warmup, splits_req=0, keep=False, skip_steps
         s_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev_s)
         s_flops = skip_steps * 4.0 * T * (kv_cache + T) * H * D
         skip = {"fps": skip_steps / el, "tflops": s_flops / (s_ms * 1e-3) / 1e12,
-                "avg_launch_ms": s_ms / skip_steps, "kv_len": kv_cache + T}
-        assert cache.stats()["frame_count"] == F + 1   # nothing appended by the skip frames
+                "avg_launch_ms": s_ms / skip_steps, "kv_len": kv_cache + T, "F": F_skip}
+        assert cache.stats()["frame_count"] == F_skip   # nothing appended by the skip frames
 
-    res = {"fps": fps, "ms_per_step": ms_per_step, "tflops": achieved_tflops,
-           "avg_launch_ms": avg_launch_ms, "flops": flops, "n_launch": n_launch,
-           "kv_lens": kv_lens, "splits": splits, "F_first": F_first, "F_last": F,
-           "app_ms": app_ms, "app_bytes": app_bytes, "append_gbps": append_gbps, "skip": skip}
+    res = {"fps": w["fps"], "ms_per_step": w["ms_per_step"], "tflops": w["tflops"],
+           "avg_launch_ms": w["avg_launch_ms"], "median_launch_ms": w["median_launch_ms"],
+           "flops": w["flops"], "n_launch": w["n_launch"], "kv_lens": w["kv_lens"],
+           "splits": w["splits"], "F_first": w["F_first"], "F_last": w["F_last"],
+           "app_ms": app_ms, "app_bytes": app_bytes, "append_gbps": append_gbps, "skip": skip,
+           "end": end}
     if keep:
-        res.update(_cache=cache, _init=init, _sets=sets, _F=F)
+        res.update(_cache=cache, _init=st.init, _sets=sets, _F=F)
     else:
         cache.close()
     return res
+
 
 def measure_batch(cfg, dev, n_streams, steps, splits_req=0, n_sets=2):
     """n_streams independent streams of ``cfg`` (distinct seeds), each filled
@@ -480,7 +569,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     m = measure_stream(cfg, dev, args.steps, args.warmup, args.splits, keep=True,
-                       skip_steps=0 if args.no_variants else args.skip_steps)
+                       skip_steps=0 if args.no_variants else args.skip_steps,
+                       end_steps=0 if args.no_windows else args.end_steps)
     B, H, D, T = cfg.num_blocks, cfg.num_heads, cfg.head_dim, cfg.tokens_per_frame
     cache, init, sets, F = m.pop("_cache"), m.pop("_init"), m.pop("_sets"), m.pop("_F")
     kv_lens, splits = m["kv_lens"], m["splits"]
@@ -582,6 +672,23 @@ def main():
             "frac": round(bt["tflops"] / PEAK_BF16_TFLOPS, 4), "peak": PEAK_BF16_TFLOPS,
             "avg_launch_ms": round(bt["avg_launch_ms"], 4)}
 
+    if not args.no_windows:
+        # the work per frame grows with the special stream (6 keys a frame):
+        # the first window, the 1000-frame stream's last frames, and the last
+        # frames of the 10,000-frame stream (4 blocks, 38% of its keys special)
+        import statistics
+        wins = {"first": window_record(m, PEAK_BF16_TFLOPS, B)}
+        if m["end"] is not None:
+            wins["stream_end"] = window_record(m["end"], PEAK_BF16_TFLOPS, B)
+        if args.long_end_steps > 0:
+            lcfg = workloads.get_config("vitl_long_stream")
+            lw = measure_end_window(lcfg, dev, args.long_end_steps, args.splits)
+            wins["long_stream_end"] = dict(window_record(lw, PEAK_BF16_TFLOPS, lcfg.num_blocks),
+                                           workload=lcfg.name)
+        fr = [w["frac"] for w in wins.values()]
+        result["windows"] = dict(wins, frac_median=round(statistics.median(fr), 4),
+                                 frac_min=min(fr), frac_max=max(fr))
+
     if args.calibrate_copy:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -595,6 +702,38 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def host_identity():
+    """The host CPU's model name (/proc/cpuinfo), the CPUs this process may
+    run on, and the BLAS library numpy calls (threadpoolctl: library, version,
+    threads, file)."""
+    import numpy  # noqa: F401  (loads the BLAS that threadpoolctl inspects)
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            i = infos[0]
+            blas = {"library": i.get("internal_api"), "version": i.get("version"),
+                    "threads": i.get("num_threads"),
+                    "file": os.path.basename(i.get("filepath") or "")}
+    except Exception:
+        pass
+    try:
+        cpus = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        cpus = os.cpu_count()
+    return {"cpu_model": model, "blas": blas, "host_cpus": cpus}
+
+
 def cpu_baseline(cfg, init, sets, F_now, budget_s):
     """The oracle as it stands, timed on this host on a bounded sample of one
     steady-state frame step: block 0, the step's 1375 query rows, h heads,
@@ -603,12 +742,8 @@ def cpu_baseline(cfg, init, sets, F_now, budget_s):
     import numpy as np
     import torch
     from oracle import StreamOracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [os.cpu_count() or 1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    ident = host_identity()
+    threads = (ident["blas"] or {}).get("threads") or os.cpu_count() or 1
 
     B, H, T = cfg.num_blocks, cfg.num_heads, cfg.tokens_per_frame
 
@@ -648,7 +783,8 @@ def cpu_baseline(cfg, init, sets, F_now, budget_s):
     per_head = (t1 + t_rest) / n_heads
     step_s = per_head * H * B
     return {"value": round(1.0 / step_s, 6), "unit": "frames/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": ident["cpu_model"], "blas": ident["blas"],
+            "host_cpus": ident["host_cpus"],
             "sample": (f"block 0, {n_heads} of {H} heads, all {T} query rows of one frame step "
                        f"at F={F_now + 1} (kv_len {98568 + 6 * (F_now + 1)}), fp64 numpy; "
                        f"{t1 + t_rest:.1f} s measured, scaled x{H * B / n_heads:.0f} to the "

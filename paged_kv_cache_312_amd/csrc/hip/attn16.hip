@@ -446,11 +446,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
       for (int e = 0; e < 16; ++e)
         s[h][kb][e] = kb * 32 + 8 * (e >> 2) + (e & 3) >= lim ? -INFINITY : s[h][kb][e];
   };
+  // Weights are kept as packed pairs of T (one 32-bit word each), so that each
+  // pair is rounded once and that one value feeds both the row sum and the
+  // PV operand.
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  auto pair_of = [&](float a, float b) __attribute__((always_inline)) {
+    return __builtin_convertvector((f32x2{a, b}), h2);  // round to nearest even
+  };
   // p = 2^(s - shift[h]) of key block kb in T, grouped as the B operand of the
   // PV MFMA (group G = 2kb + g holds elements 8g..8g+7 of s[h][kb]); lt[h]
   // receives this lane's sum of the rounded p (exactly the weights the PV
   // product uses)
-  auto exp_block = [&](auto nh_c, const f32x16 (*s)[2], int kb, const float* shift, h8 (*pb)[4],
+  auto exp_block = [&](auto nh_c, const f32x16 (*s)[2], int kb, const float* shift, u32x4 (*pb)[4],
                        float* lt) __attribute__((always_inline)) {
     constexpr int NH = decltype(nh_c)::value;
 #pragma unroll
@@ -458,34 +466,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
       lt[h] = 0.f;
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        h8 v;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = static_cast<T>(fast_exp2(s[h][kb][8 * g + u] - shift[h]));
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const h2 pr = {v[2 * u], v[2 * u + 1]};
+          const h2 pr = pair_of(fast_exp2(s[h][kb][8 * g + 2 * u] - shift[h]),
+                                fast_exp2(s[h][kb][8 * g + 2 * u + 1] - shift[h]));
           lt[h] = Elt<T>::dot2(pr, ones, lt[h]);
+          pb[h][2 * kb + g][u] = __builtin_bit_cast(uint32_t, pr);
         }
-        pb[h][2 * kb + g] = v;
       }
     }
   };
   // four of exp_block's weights: elements 4q .. 4q+3 of s[h][kb], added to lt
-  auto exp_part = [&](const f32x16 (*s)[2], int h, int kb, int q, h8 (*pb)[4], float* lt)
+  auto exp_part = [&](const f32x16 (*s)[2], int h, int kb, int q, u32x4 (*pb)[4], float* lt)
                       __attribute__((always_inline)) {
-    h8& v = pb[h][2 * kb + (q >> 1)];
-    const int o4 = 4 * (q & 1);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) v[o4 + u] = static_cast<T>(fast_exp2(s[h][kb][4 * q + u]));
+    u32x4& v = pb[h][2 * kb + (q >> 1)];
+    const int o2 = 2 * (q & 1);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const h2 pr = {v[o4 + 2 * u], v[o4 + 2 * u + 1]};
+      const h2 pr = pair_of(fast_exp2(s[h][kb][4 * q + 2 * u]), fast_exp2(s[h][kb][4 * q + 2 * u + 1]));
       lt[h] = Elt<T>::dot2(pr, ones, lt[h]);
+      v[o2 + u] = __builtin_bit_cast(uint32_t, pr);
     }
   };
+  auto as_h8 = [&](const u32x4& w) __attribute__((always_inline)) { return __builtin_bit_cast(h8, w); };
   // O^T[d][row] += V^T[d][keys] P^T[keys][row] over key block kb; each V
   // operand read feeds every half's MFMA
-  auto pv_block = [&](auto nh_c, const uint16_t* V, int kb, const h8 (*pb)[4]) __attribute__((always_inline)) {
+  auto pv_block = [&](auto nh_c, const uint16_t* V, int kb, const u32x4 (*pb)[4]) __attribute__((always_inline)) {
     constexpr int NH = decltype(nh_c)::value;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
@@ -494,7 +500,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
         const uint16_t* p = V + (db == 0 ? v_rd0 : v_rd1) + (16 * G) * LS;
         const h8 vf = v_operand<h8>(p, p + 8 * LS);
 #pragma unroll
-        for (int h = 0; h < NH; ++h) o[h][db] = Elt<T>::mfma(vf, pb[h][G], o[h][db]);
+        for (int h = 0; h < NH; ++h) o[h][db] = Elt<T>::mfma(vf, as_h8(pb[h][G]), o[h][db]);
       }
   };
   // the row's max over key blocks kb0 .. kb1 minus m_run (both lanes of the
@@ -541,7 +547,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     const uint16_t* K = lds_k[stage];
     const uint16_t* V = lds_v[stage];
     f32x16 s[2][2];
-    h8 pb[2][4];
+    u32x4 pb[2][4];
     float lt0[2], lt1[2];
     // scores against a running max of 0 (the rare path below corrects a
     // biased wavefront's)
@@ -632,7 +638,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
       const int mi = st / NH, h = st % NH;
       const int db = mi >> 1, G = mi & 1;
       exp_part(s, st >> 2, 1, st & 3, pb, lt1);
-      o[h][db] = Elt<T>::mfma(vf0[2 * db + G], pb[h][G], o[h][db]);
+      o[h][db] = Elt<T>::mfma(vf0[2 * db + G], as_h8(pb[h][G]), o[h][db]);
       __builtin_amdgcn_sched_barrier(0);
     }
     jump = false;

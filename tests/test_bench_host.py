@@ -88,3 +88,20 @@ def test_append_traffic_follows_the_append_sources(tmp_path, monkeypatch):
     path.write_text("header\n" + json.dumps(dict(rec, append_source_hash="1" * 16)))
     assert bench.recorded_append_traffic() is None
     assert bench.kernel_source_hash(sources=bench.APPEND_SOURCES) != bench.kernel_source_hash()
+
+
+def test_host_identity_names_the_cpu_and_the_blas():
+    ident = bench.host_identity()
+    assert set(ident) == {"cpu_model", "blas", "host_cpus"}
+    assert ident["host_cpus"] >= 1
+    if ident["blas"] is not None:
+        assert ident["blas"]["threads"] >= 1 and ident["blas"]["library"]
+
+
+def test_window_record():
+    w = {"F_first": 981, "F_last": 1000, "kv_lens": [104448, 104562], "fps": 70.0,
+         "ms_per_step": 14.2857, "tflops": 1000.0, "avg_launch_ms": 0.58,
+         "median_launch_ms": 0.579, "splits": 8}
+    r = bench.window_record(w, 2516.6, 24)
+    assert r["timed_frames"] == [981, 1000] and r["kv_len"] == [104448, 104562]
+    assert r["frac"] == round(1000.0 / 2516.6, 4) and r["blocks"] == 24
