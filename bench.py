@@ -1,9 +1,11 @@
 """Frame-step throughput of the 24-block ViT-L-shaped stream on one MI355X.
 
-One step = one new frame through all 24 blocks: per block, append its K/V
-(HIP scatter), evict and plan once (host; one small table upload), and paged
-attention (HIP, bf16 MFMA).  Shapes: 1369 patch + 6 special tokens per frame,
-16 heads x 64, scale_frames 8, sliding_window 64, bf16 unit-normal inputs.
+One step = one new frame through all 24 blocks: per block, one
+lbm_append_run (block 0 also reserves, plans -- one small table upload and
+the row-table kernel -- and evicts): one launch of paged attention (HIP,
+bf16 MFMA) whose extra workgroups copy the block's K/V rows into their
+pages.  Shapes: 1369 patch + 6 special tokens per frame, 16 heads x 64,
+scale_frames 8, sliding_window 64, bf16 unit-normal inputs.
 
 Setup (untimed): the 8-frame first step and 64 single frames (F = 72, the
 window full), then W warm-up steps; then K timed steps (the first window,
@@ -213,10 +215,12 @@ class Stream:
     """One synthetic stream of ``cfg`` in a live cache: the first step, then
     single frames drawn from N_INPUT_SETS seeded input sets per block (resident
     in HBM, cycled).  A frame step appends every block's rows, evicts and
-    plans once (at block 0) and runs attention per block; a fast-forward step
-    (``run=False``) appends and evicts only."""
+    plans once (at block 0) and runs attention per block: with ``fused``, one
+    lbm_append_run per block (append and attention in one launch), else
+    lbm_append_frame, lbm_evict_frames, lbm_plan and lbm_run.  A fast-forward
+    step (``run=False``) appends and evicts only."""
 
-    def __init__(self, cfg, dev, splits_req=0):
+    def __init__(self, cfg, dev, splits_req=0, fused=True):
         import torch
 
         import paged_kv_cache_312_amd as lbm
@@ -233,10 +237,20 @@ class Stream:
         self.outs = [torch.empty((T, H, D), dtype=self.cache.dtype, device=dev) for _ in range(B)]
         self.F = 0
         self.step_idx = 0
+        self.fused = fused
         torch.cuda.synchronize()
 
     def frame_step(self, inputs, out_bufs, nq, ev=None, ev_block=-1, run=True):
         cache = self.cache
+        if run and self.fused:
+            for b in range(self.cfg.num_blocks):
+                q, k, v = inputs[b]
+                if b == ev_block:
+                    ev[0].record(self.stream)
+                cache.append_run(b, q, k, v, out_bufs[b])
+                if b == ev_block:
+                    ev[1].record(self.stream)
+            return
         for b in range(self.cfg.num_blocks):
             q, k, v = inputs[b]
             cache.append_frame(b, k, v)
@@ -274,10 +288,11 @@ class Stream:
 
     def window(self, steps):
         """Time ``steps`` frame steps: wall clock over the whole steps, and HIP
-        events on the launch stream around one lbm_run per step (block i mod B
-        of step i: every block's launch has the same shape within a step, and
-        an event pair at every launch would itself add ~6 us of queue work per
-        event to the steps being timed)."""
+        events on the launch stream around one attention launch per step
+        (block i mod B of step i, or 1 + i mod (B-1) with fused calls: every
+        block's launch has the same shape within a step, and an event pair at
+        every launch would itself add ~6 us of queue work per event to the
+        steps being timed)."""
         import statistics
 
         import torch
@@ -290,7 +305,10 @@ class Stream:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            self.frame_step(self.sets[self.step_idx % N_INPUT_SETS], self.outs, T, ev[i], i % B)
+            # with fused calls block 0's call also plans (table upload, row
+            # table kernel) before its launch: bracket the other blocks
+            eb = 1 + i % (B - 1) if self.fused and B > 1 else i % B
+            self.frame_step(self.sets[self.step_idx % N_INPUT_SETS], self.outs, T, ev[i], eb)
             self.F += 1
             self.step_idx += 1
             # past the window fill every frame adds special_per_frame keys
@@ -322,10 +340,10 @@ def window_record(w, peak, blocks):
             "median_launch_ms": round(w["median_launch_ms"], 4), "key_splits": w["splits"]}
 
 
-def measure_end_window(cfg, dev, steps, splits_req=0):
+def measure_end_window(cfg, dev, steps, splits_req=0, fused=True):
     """The last ``steps`` frames of ``cfg``'s stream: the frames before them
     only append and evict (no attention), then the timed window."""
-    s = Stream(cfg, dev, splits_req)
+    s = Stream(cfg, dev, splits_req, fused)
     try:
         s.first(run=False)
         s.advance(cfg.total_frames - steps - s.F, run=False)
@@ -335,7 +353,7 @@ def measure_end_window(cfg, dev, steps, splits_req=0):
 
 
 def measure_stream(cfg, dev, steps, warmup, splits_req=0, keep=False, skip_steps=0,
-                   end_steps=0):
+                   end_steps=0, fused=True):
     """Stream ``cfg`` through its first step and the window fill, ``warmup``
     more steps, then time ``steps`` frame steps (all blocks: append, evict and
     plan once, attention) and one event pair around the appends of blocks
@@ -347,7 +365,7 @@ def measure_stream(cfg, dev, steps, warmup, splits_req=0, keep=False, skip_steps
     import torch
 
     B, H, D, T = cfg.num_blocks, cfg.num_heads, cfg.head_dim, cfg.tokens_per_frame
-    st = Stream(cfg, dev, splits_req)
+    st = Stream(cfg, dev, splits_req, fused)
     cache, stream, sets, outs = st.cache, st.stream, st.sets, st.outs
     st.first()
     st.advance(cfg.scale_frames + cfg.sliding_window - st.F)
@@ -602,13 +620,20 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(),
-                     "kernel": "attn_d64_kernel<__bf16> (+ merge_kernel): one lbm_run",
+                     "kernel": "attn_d64_kernel<__bf16> (+ merge_kernel): one lbm_append_run "
+                               "(attention with the block's append carried by extra workgroups)",
                      "avg_launch_ms": round(avg_launch_ms, 4),
                      "flops_per_launch_avg": flops / n_launch},
-        "append": {"bound": "hbm", "achieved": round(append_gbps, 1), "peak": PEAK_HBM_GBPS,
-                   "unit": "GB/s", "frac": round(append_gbps / PEAK_HBM_GBPS, 4),
-                   "traffic": recorded_append_traffic(),
-                   "avg_launch_ms": round(app_ms, 5), "bytes_per_launch": app_bytes},
+        # the timed steps carry each block's append inside its attention
+        # launch (lbm_append_run); the separate append kernel (lbm_append_frame)
+        # is timed on one more step for reference, and the whole step made of
+        # separate calls is a variant below
+        "append": {"mode": "fused into the attention launch",
+                   "separate_kernel": {
+                       "bound": "hbm", "achieved": round(append_gbps, 1), "peak": PEAK_HBM_GBPS,
+                       "unit": "GB/s", "frac": round(append_gbps / PEAK_HBM_GBPS, 4),
+                       "traffic": recorded_append_traffic(),
+                       "avg_launch_ms": round(app_ms, 5), "bytes_per_launch": app_bytes}},
     }
 
     cache.close()
@@ -620,6 +645,17 @@ def main():
             "frac": round(sk["tflops"] / PEAK_BF16_TFLOPS, 4), "peak": PEAK_BF16_TFLOPS,
             "avg_launch_ms": round(sk["avg_launch_ms"], 4)}}
     if not args.no_variants:
+        # the same stream made of separate calls per block (lbm_append_frame,
+        # then lbm_run; evict and plan once): the append kernel's launches are
+        # back in the step
+        v = measure_stream(cfg, dev, args.variant_steps, args.warmup, args.splits, fused=False)
+        result.setdefault("variants", {})["separate_calls_bf16"] = {
+            "value": round(v["fps"], 3), "unit": "frames/s", "steps": args.variant_steps,
+            "ms_per_step": round(v["ms_per_step"], 4),
+            "timed_frames": [v["F_first"], v["F_last"]],
+            "attention_tflops": round(v["tflops"], 2),
+            "frac": round(v["tflops"] / PEAK_BF16_TFLOPS, 4), "peak": PEAK_BF16_TFLOPS,
+            "avg_launch_ms": round(v["avg_launch_ms"], 4), "key_splits": v["splits"]}
         # the same 24-block stream with fp16 storage and MFMA (the pages' other
         # 16-bit type); a shorter timed run after the same fill
         v = measure_stream(cfg.replace(dtype="f16"), dev, args.variant_steps, args.warmup,

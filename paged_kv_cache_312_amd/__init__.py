@@ -20,7 +20,7 @@ __all__ = [
     "lbm_query_sizes", "lbm_cache_create", "lbm_cache_destroy", "lbm_cache_reset",
     "lbm_cache_seed_free_lists", "lbm_append_frame", "lbm_evict_frames",
     "lbm_rollback_last_frame", "lbm_plan", "lbm_run", "lbm_plan_transient", "lbm_run_transient",
-    "lbm_run_batch", "MAX_BATCH", "lbm_graph_create", "lbm_graph_launch", "lbm_graph_destroy",
+    "lbm_append_run", "lbm_run_batch", "MAX_BATCH", "lbm_graph_create", "lbm_graph_launch", "lbm_graph_destroy",
     "lbm_graph_num_splits", "StepGraph",
     "lbm_paged_attention", "lbm_paged_attention_static", "lbm_get_stats",
     "lbm_dump_state", "lbm_get_plan", "lbm_plan_num_splits", "lbm_last_error",
@@ -133,6 +133,13 @@ def lbm_run_transient(handle: int, block_idx: int, q: int, k: int, v: int, out: 
     _ck(lib().lbm_run_transient(c_void_p(handle), block_idx, c_void_p(q), c_void_p(k),
                                 c_void_p(v), c_void_p(out), num_q_tokens, c_void_p(stream)),
         "lbm_run_transient")
+
+
+def lbm_append_run(handle: int, block_idx: int, q: int, k: int, v: int, out: int,
+                   num_frames: int, num_q_tokens: int, stream: int) -> None:
+    _ck(lib().lbm_append_run(c_void_p(handle), block_idx, c_void_p(q), c_void_p(k), c_void_p(v),
+                             c_void_p(out), num_frames, num_q_tokens, c_void_p(stream)),
+        "lbm_append_run")
 
 
 MAX_BATCH = 8
@@ -323,6 +330,23 @@ class PagedKVCache:
             self._check_tensor(out, q.shape[0])
         lbm_run_transient(self.handle, block_idx, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                           out.data_ptr(), q.shape[0], self._stream(stream))
+        return out
+
+    def append_run(self, block_idx: int, q, k, v, out=None, stream=None):
+        """One block's append and attention of a frame step in one launch
+        (block 0 also reserves, plans for q's rows and evicts); returns out."""
+        T = self.cfg.patches_per_frame + self.cfg.special_per_frame
+        nf = k.shape[0] // T
+        self._check_tensor(k, nf * T)
+        self._check_tensor(v, nf * T)
+        self._check_tensor(q)
+        if out is None:
+            out = self.torch.empty_like(q)
+        else:
+            self._check_tensor(out, q.shape[0])
+        self._own_rows = None
+        lbm_append_run(self.handle, block_idx, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                       out.data_ptr(), nf, q.shape[0], self._stream(stream))
         return out
 
     def capture_step(self, num_frames: int, ks, vs, qs, outs) -> "StepGraph":

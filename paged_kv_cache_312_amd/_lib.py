@@ -68,6 +68,8 @@ LBM_FUNCS = {
     "lbm_graph_destroy": (None, [c_void_p]),
     "lbm_run_transient": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_int32, c_void_p]),
+    "lbm_append_run": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_int32, c_int32, c_void_p]),
     "lbm_paged_attention": (c_int32, [POINTER(LbmConfig), c_void_p, c_void_p, c_int32, c_void_p,
                                       c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p,
                                       c_void_p]),

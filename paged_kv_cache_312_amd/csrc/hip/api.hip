@@ -92,6 +92,7 @@ struct lbm_cache {
   int32_t plan_q = 0;
   int32_t plan_splits = 0;
   int32_t plan_own = 0;       // own rows of a skip-append step planned (0: a normal plan)
+  bool plan_fused = false;    // the own rows are the open step's frames (lbm_append_run)
   PlanInfo plan;
 
   // pinned staging of the table, double-buffered and guarded by events
@@ -190,7 +191,7 @@ AttnArgs base_args(const lbm_config& c, const void* q, void* out, int32_t nq, co
 // c's head_dim and dtype, all with or all without own rows), then the merge
 // of every stream whose key range is split.
 lbm_status launch_attention_batch(const lbm_config& c, AttnArgs* as, int32_t n, int32_t splits,
-                                  hipStream_t st) {
+                                  hipStream_t st, const FusedAppend* app = nullptr) {
   BatchArgs b;
   std::memset(&b, 0, sizeof(b));
   b.n = n;
@@ -201,6 +202,10 @@ lbm_status launch_attention_batch(const lbm_config& c, AttnArgs* as, int32_t n, 
   }
   b.total_items = b.item_start[n];
   b.items_per_xcd = (b.total_items + 7) / 8;
+  if (app) {
+    b.app = *app;
+    b.app.wg0 = 8 * b.items_per_xcd;
+  }
   const bool own = as[0].tr_start < as[0].kv_len;
   hipError_t e = c.dtype == LBM_F32 ? launch_attn_f32(b, c.head_dim, own, st)
                                     : launch_attn16(b, c.head_dim, c.dtype == LBM_F16, own, st);
@@ -214,8 +219,9 @@ lbm_status launch_attention_batch(const lbm_config& c, AttnArgs* as, int32_t n, 
   return LBM_OK;
 }
 
-lbm_status launch_attention(const lbm_config& c, AttnArgs* a, int32_t splits, hipStream_t st) {
-  return launch_attention_batch(c, a, 1, splits, st);
+lbm_status launch_attention(const lbm_config& c, AttnArgs* a, int32_t splits, hipStream_t st,
+                            const FusedAppend* app = nullptr) {
+  return launch_attention_batch(c, a, 1, splits, st, app);
 }
 
 }  // namespace
@@ -391,7 +397,9 @@ lbm_status lbm_cache_create(const lbm_config* cfg, void* const* patch_pools,
   c->num_cu = ncu > 0 ? ncu : 256;
   c->wg_per_cu = attn_occupancy(cfg->dtype, cfg->head_dim);
 
-  c->staging_bytes = c->ws.special_ids_off - c->ws.patch_ids_off +
+  // staging = workspace [desc_off, special ids end): the step descriptor (a
+  // fused append's pages), then the tables
+  c->staging_bytes = c->ws.special_ids_off - c->ws.desc_off +
                      sizeof(int32_t) * size_t(std::max(1, cfg->max_special_pages));
   for (int i = 0; i < 2; ++i) {
     e = hipHostMalloc(reinterpret_cast<void**>(&c->staging[i]), c->staging_bytes,
@@ -522,32 +530,58 @@ namespace {
 
 // The plan of a frame step: the visible set of the cache as it stands, plus
 // `own` rows of the frame itself on a skip-append step (they follow the
-// special stream).
-lbm_status plan_impl(lbm_cache* c, int32_t num_q_tokens, int32_t own, void* hip_stream) {
+// special stream).  fused_nf > 0: the plan of lbm_append_run for the open
+// step of fused_nf frames: the visible set without the step's own rows (its
+// patch pages are the last fused_nf visible pages, its specials the last
+// fused_nf * S special tokens), which the attention reads from the caller's
+// rows instead; the step descriptor carries the pages the launches write.
+lbm_status plan_impl(lbm_cache* c, int32_t num_q_tokens, int32_t own, void* hip_stream,
+                     int32_t fused_nf = 0) {
   if (num_q_tokens < 1 || num_q_tokens > c->cfg.max_q_tokens)
     return fail(LBM_ERR_INVALID_ARG, "num_q_tokens %d outside 1..%d", num_q_tokens,
                 c->cfg.max_q_tokens);
   if (c->bk.empty()) return fail(LBM_ERR_BAD_STATE, "plan on an empty cache");
-  const PlanInfo p = c->bk.plan_info();
+  PlanInfo p = c->bk.plan_info();
   if (p.kv_len < 1) return fail(LBM_ERR_BAD_STATE, "no visible tokens");
+  std::vector<int32_t> pp;
+  c->bk.visible_patch_pages(&pp);
+  StepDesc d;
+  if (fused_nf > 0) {
+    const WriteMap& wm = c->bk.write_map();
+    const int32_t T = c->cfg.patches_per_frame + c->cfg.special_per_frame;
+    bool tail = wm.nf == fused_nf && int32_t(pp.size()) >= fused_nf &&
+                p.special_tokens >= fused_nf * c->cfg.special_per_frame;
+    for (int32_t f = 0; tail && f < fused_nf; ++f)
+      tail = pp[pp.size() - size_t(fused_nf) + size_t(f)] == wm.patch_pages[f];
+    if (!tail) return fail(LBM_ERR_BAD_STATE, "the step's frames are not the newest visible ones");
+    own = fused_nf * T;
+    p.patch_tokens -= fused_nf * c->cfg.patches_per_frame;
+    p.kv_len -= own;
+    d.st0 = wm.st0;
+    d.sp_first = wm.sp_first;
+    for (int32_t f = 0; f < wm.nf; ++f) d.patch_pages[f] = wm.patch_pages[f];
+    for (int32_t j = 0; j < wm.n_sp; ++j) d.spages[j] = wm.spages[j];
+  }
 
-  // stage [patch ids | pad | special ids] exactly as laid out in the workspace
+  // stage [desc | patch ids | pad | special ids] exactly as laid out in the
+  // workspace; the descriptor travels only with a fused plan
   const int i = c->staging_next;
   if (c->staging_pending[i]) {
     const hipError_t e = hipEventSynchronize(c->staging_ev[i]);
     if (e != hipSuccess) return hip_fail(e, "staging wait");
     c->staging_pending[i] = false;
   }
-  std::vector<int32_t> pp;
-  c->bk.visible_patch_pages(&pp);
   char* stg = reinterpret_cast<char*>(c->staging[i]);
-  std::memcpy(stg, pp.data(), sizeof(int32_t) * pp.size());
-  const size_t sp_off = c->ws.special_ids_off - c->ws.patch_ids_off;
+  const size_t pp_off = c->ws.patch_ids_off - c->ws.desc_off;
+  const size_t sp_off = c->ws.special_ids_off - c->ws.desc_off;
+  if (fused_nf > 0) std::memcpy(stg, &d, sizeof(d));
+  std::memcpy(stg + pp_off, pp.data(), sizeof(int32_t) * pp.size());
   const std::vector<int32_t>& sp = c->bk.special_pages();
   if (!sp.empty()) std::memcpy(stg + sp_off, sp.data(), sizeof(int32_t) * sp.size());
-  const size_t bytes = sp_off + sizeof(int32_t) * sp.size();
+  const size_t from = fused_nf > 0 ? 0 : pp_off;
+  const size_t bytes = sp_off + sizeof(int32_t) * sp.size() - from;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  hipError_t e = hipMemcpyAsync(c->workspace + c->ws.patch_ids_off, stg, bytes,
+  hipError_t e = hipMemcpyAsync(c->workspace + c->ws.desc_off + from, stg + from, bytes,
                                 hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipEventRecord(c->staging_ev[i], s);
   if (e != hipSuccess) return hip_fail(e, "table upload");
@@ -568,6 +602,7 @@ lbm_status plan_impl(lbm_cache* c, int32_t num_q_tokens, int32_t own, void* hip_
   c->plan_q = num_q_tokens;
   c->plan_splits = ns;
   c->plan_own = own;
+  c->plan_fused = fused_nf > 0;
   c->plan_epoch = c->bk.epoch();
   c->plan_valid = true;
   return LBM_OK;
@@ -618,7 +653,8 @@ lbm_status lbm_run(lbm_cache* c, int32_t block_idx, const void* q, void* out,
     return fail(LBM_ERR_BAD_STATE, "run with %d queries, plan made for %d", num_q_tokens, c->plan_q);
   if (c->step_open && !c->appended[size_t(block_idx)])
     return fail(LBM_ERR_BAD_STATE, "block %d has not appended the open step", block_idx);
-  if (c->plan_own > 0) return fail(LBM_ERR_BAD_STATE, "the plan is a skip-append plan");
+  if (c->plan_own > 0)
+    return fail(LBM_ERR_BAD_STATE, "the plan is a skip-append or a fused append plan");
   AttnArgs a = base_args(c->cfg, q, out, num_q_tokens, c->patch_pools[size_t(block_idx)],
                          c->special_pools[size_t(block_idx)],
                          reinterpret_cast<const uint32_t*>(c->workspace + c->ws.rowtab_off),
@@ -640,7 +676,8 @@ lbm_status lbm_run_transient(lbm_cache* c, int32_t block_idx, const void* q, con
   if (!c->plan_valid) return fail(LBM_ERR_BAD_STATE, "run without a plan");
   if (c->plan_epoch != c->bk.epoch())
     return fail(LBM_ERR_BAD_STATE, "plan is stale (append, evict or rollback since)");
-  if (c->plan_own < 1) return fail(LBM_ERR_BAD_STATE, "the plan is not a skip-append plan");
+  if (c->plan_own < 1 || c->plan_fused)
+    return fail(LBM_ERR_BAD_STATE, "the plan is not a skip-append plan");
   if (num_q_tokens != c->plan_q)
     return fail(LBM_ERR_BAD_STATE, "run with %d queries, plan made for %d", num_q_tokens, c->plan_q);
   AttnArgs a = base_args(c->cfg, q, out, num_q_tokens, c->patch_pools[size_t(block_idx)],
@@ -652,6 +689,102 @@ lbm_status lbm_run_transient(lbm_cache* c, int32_t block_idx, const void* q, con
   a.tk = k;
   a.tv = v;
   return launch_attention(c->cfg, &a, c->plan_splits, static_cast<hipStream_t>(hip_stream));
+}
+
+lbm_status lbm_append_run(lbm_cache* c, int32_t block_idx, const void* q, const void* k,
+                          const void* v, void* out, int32_t num_frames, int32_t num_q_tokens,
+                          void* hip_stream) {
+  clear_error();
+  lbm_status st = check_live(c);
+  if (st != LBM_OK) return st;
+  if (block_idx < 0 || block_idx >= c->cfg.num_blocks)
+    return fail(LBM_ERR_INVALID_ARG, "block_idx %d outside 0..%d", block_idx, c->cfg.num_blocks - 1);
+  if (!q || !out || !k || !v || !aligned16(q) || !aligned16(out) || !aligned16(k) || !aligned16(v))
+    return fail(LBM_ERR_INVALID_ARG, "q/k/v/out null or not 16-byte aligned");
+  if (num_frames < 1 || num_frames > c->cfg.max_frames_per_step)
+    return fail(LBM_ERR_INVALID_ARG, "num_frames %d outside 1..%d", num_frames,
+                c->cfg.max_frames_per_step);
+  if (num_frames > c->cfg.sliding_window)
+    return fail(LBM_ERR_INVALID_ARG, "num_frames %d beyond the window of %d frames", num_frames,
+                c->cfg.sliding_window);
+  if (num_q_tokens < 1 || num_q_tokens > c->cfg.max_q_tokens)
+    return fail(LBM_ERR_INVALID_ARG, "num_q_tokens %d outside 1..%d", num_q_tokens,
+                c->cfg.max_q_tokens);
+  const int32_t T = c->cfg.patches_per_frame + c->cfg.special_per_frame;
+  if (int64_t(num_frames) * T > c->cfg.max_q_tokens)
+    return fail(LBM_ERR_INVALID_ARG, "%d frames of %d tokens exceed max_q_tokens %d", num_frames,
+                T, c->cfg.max_q_tokens);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (block_idx == 0) {
+    if (c->step_open) {
+      for (int32_t b = 0; b < c->cfg.num_blocks; ++b)
+        if (!c->appended[size_t(b)])
+          return fail(LBM_ERR_BAD_STATE, "block %d has not appended the previous step", b);
+    }
+    const bool was_open = c->step_open;
+    const int32_t was_nf = c->step_nf;
+    st = c->bk.reserve(num_frames);
+    if (st != LBM_OK) return st;
+    // the visible set after this step's eviction; eviction itself follows the
+    // plan, as in the graph step, so that a refused plan can still be undone
+    st = plan_impl(c, num_q_tokens, 0, hip_stream, num_frames);
+    if (st != LBM_OK) {
+      // as before the call (the previous step, if any, was complete)
+      if (num_frames != 1 || c->bk.rollback() != LBM_OK) c->poisoned = true;
+      c->step_open = was_open;
+      c->step_nf = was_nf;
+      return st;
+    }
+    c->step_open = true;
+    c->step_nf = num_frames;
+    std::fill(c->appended.begin(), c->appended.end(), 0);
+    std::vector<int32_t> evicted;
+    st = c->bk.evict(&evicted);
+    if (st != LBM_OK) {
+      c->poisoned = true;
+      return st;
+    }
+    c->plan_epoch = c->bk.epoch();
+  } else {
+    if (!c->step_open) return fail(LBM_ERR_BAD_STATE, "block %d appends before block 0", block_idx);
+    if (c->appended[size_t(block_idx)])
+      return fail(LBM_ERR_BAD_STATE, "block %d already appended this step", block_idx);
+    if (num_frames != c->step_nf)
+      return fail(LBM_ERR_INVALID_ARG, "block %d appends %d frames, block 0 appended %d",
+                  block_idx, num_frames, c->step_nf);
+    if (!c->plan_valid || !c->plan_fused || c->plan_epoch != c->bk.epoch())
+      return fail(LBM_ERR_BAD_STATE, "the open step was not opened by lbm_append_run");
+    if (num_q_tokens != c->plan_q)
+      return fail(LBM_ERR_BAD_STATE, "run with %d queries, plan made for %d", num_q_tokens,
+                  c->plan_q);
+  }
+  AttnArgs a = base_args(c->cfg, q, out, num_q_tokens, c->patch_pools[size_t(block_idx)],
+                         c->special_pools[size_t(block_idx)],
+                         reinterpret_cast<const uint32_t*>(c->workspace + c->ws.rowtab_off),
+                         c->workspace, c->ws);
+  a.tr_start = c->plan.kv_len;
+  a.kv_len = c->plan.kv_len + c->plan_own;
+  a.tk = k;
+  a.tv = v;
+  FusedAppend f;
+  std::memset(&f, 0, sizeof(f));
+  f.k = static_cast<const uint4*>(k);
+  f.v = static_cast<const uint4*>(v);
+  f.patch_pool = static_cast<uint4*>(c->patch_pools[size_t(block_idx)]);
+  f.special_pool = static_cast<uint4*>(c->special_pools[size_t(block_idx)]);
+  f.desc = reinterpret_cast<const StepDesc*>(c->workspace + c->ws.desc_off);
+  f.rows = num_frames * T;
+  f.T = T;
+  f.P = c->cfg.patches_per_frame;
+  f.S = c->cfg.special_per_frame;
+  f.SPS = c->cfg.special_page_size;
+  f.rc = int32_t(size_t(c->cfg.num_heads) * c->cfg.head_dim * dtype_size(c->cfg.dtype) / 16);
+  // about 16 rows of K or V per workgroup, at most 256 workgroups
+  f.wgs = std::max(1, std::min(256, (2 * f.rows + 15) / 16));
+  st = launch_attention(c->cfg, &a, c->plan_splits, s, &f);
+  if (st != LBM_OK) return st;
+  c->appended[size_t(block_idx)] = 1;
+  return LBM_OK;
 }
 
 lbm_status lbm_run_batch(lbm_cache* const* caches, int32_t n, int32_t block_idx,

@@ -196,6 +196,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[NST][TILE];
   __shared__ __attribute__((aligned(16))) uint32_t lds_code[NCODE][64];
 
+  if (b.app.wgs > 0 && int32_t(blockIdx.x) >= b.app.wg0) {
+    // a workgroup of an append carried by this launch
+    fused_append_wg(b.app, int32_t(blockIdx.x) - b.app.wg0);
+    return;
+  }
   int32_t sid;
   const int32_t item = work_item(b, blockIdx.x, sid);
   if (sid < 0) return;
@@ -302,11 +307,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     const char* base = special ? col_base[1][v] : col_base[0][v];
     return base + (code & 0x7fffffffu);
   };
-  // K and V of tile position x into stage x mod NST.  Skip-append step: keys
-  // in [tr_start, kv_len) come from the frame's own rows (the row table holds
-  // position 0's code there, like the padding past kv_len, which keeps its
-  // code); the test is uniform per tile, and only the step's last tiles take
-  // that branch.
+  // K and V of tile position x into stage x mod NST.  Skip-append step (and
+  // a fused append): keys in [tr_start, kv_len) come from the frame's own rows
+  // (the row table holds position 0's code there), and so does the padding
+  // past kv_len; the test is uniform per tile, and only the step's last tiles
+  // take that branch.
   auto load_kv = [&](int32_t x, uint2 c) __attribute__((always_inline)) {
     const int32_t stage = x & (NST - 1);
     const char* k0 = row_ptr(c.x, false);
@@ -317,15 +322,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     if (TR && t0 + 64 > a.tr_start) {
       const char* tk = static_cast<const char*>(a.tk) + k_col;
       const char* tv = static_cast<const char*>(a.tv) + v_col;
+      // the padding past kv_len repeats the last own row (finite input, whose
+      // weights the mask zeroes; a pool row there may be unwritten memory
+      // when every key of the step is the frame's own)
       const int32_t j0 = t0 + lp - a.tr_start, j1 = j0 + 32;
       const int32_t n_own = a.kv_len - a.tr_start;
-      if (j0 >= 0 && j0 < n_own) {
-        k0 = tk + size_t(j0) * a.row_bytes;
-        v0 = tv + size_t(j0) * a.row_bytes;
+      if (j0 >= 0) {
+        const int32_t j = min(j0, n_own - 1);
+        k0 = tk + size_t(j) * a.row_bytes;
+        v0 = tv + size_t(j) * a.row_bytes;
       }
-      if (j1 >= 0 && j1 < n_own) {
-        k1 = tk + size_t(j1) * a.row_bytes;
-        v1 = tv + size_t(j1) * a.row_bytes;
+      if (j1 >= 0) {
+        const int32_t j = min(j1, n_own - 1);
+        k1 = tk + size_t(j) * a.row_bytes;
+        v1 = tv + size_t(j) * a.row_bytes;
       }
     }
     load_to_lds<16>(k0, &lds_k[stage][(8 * wave) * LS]);
@@ -763,7 +773,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
 hipError_t launch_attn16(const BatchArgs& b, int32_t head_dim, bool fp16, bool transient,
                          hipStream_t stream) {
   if (head_dim != 64) return hipErrorInvalidValue;
-  const dim3 grid(8 * b.items_per_xcd), block(kThreads);
+  const dim3 grid(8 * b.items_per_xcd + b.app.wgs), block(kThreads);
   if (fp16 && transient)
     hipLaunchKernelGGL((attn_d64_kernel<_Float16, true>), grid, block, 0, stream, b);
   else if (fp16)

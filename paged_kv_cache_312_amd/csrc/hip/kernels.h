@@ -30,7 +30,8 @@ hipError_t launch_append(const AppendArgs& a, int32_t nf, hipStream_t stream);
 // Row table of a frame step: for each key position j of the visible set, the
 // byte offset of K[j][head 0][0] inside its block's pool, with bit 31 set for
 // the special pool.  Positions past kv_len (up to whole 64-key tiles) repeat
-// position 0, whose scores the attention kernel masks.
+// position 0, whose scores the attention kernel masks (row 0 of patch page 0
+// when kv_len is 0: every key of the step read from the caller's rows).
 struct RowtabArgs {
   const int32_t* patch_ids;   // visible patch pages, in table order
   const int32_t* special_ids; // special pages, in order
@@ -84,12 +85,31 @@ struct AttnArgs {
 // the work items of stream s are [item_start[s], item_start[s+1]) of the
 // launch's item range, each stream's laid out as a single-stream launch's.
 constexpr int kMaxBatch = 8;
+
+// An append carried by an attention launch: workgroups [wg0, wg0 + wgs) of
+// the grid copy one block's rows of the step into their pages, with the
+// placement of append_scatter_kernel, instead of computing attention.  The
+// launch's attention reads those rows from k / v (the skip-append address
+// form), so no workgroup reads a row that another one writes.  wgs = 0: none.
+struct FusedAppend {
+  const uint4* k;             // [rows][rc]
+  const uint4* v;
+  uint4* patch_pool;          // [pages][2][P][rc]
+  uint4* special_pool;        // [pages][2][SPS][rc]
+  const StepDesc* desc;       // st0, sp_first and the step's pages
+  int32_t rows;               // nf * T
+  int32_t T, P, S, SPS;
+  int32_t rc;                 // 16-byte chunks per token row
+  int32_t wg0, wgs;
+};
+
 struct BatchArgs {
   int32_t n;
   int32_t total_items;        // item_start[n]
   int32_t items_per_xcd;      // ceil(total_items / 8)
   int32_t item_start[kMaxBatch + 1];
   AttnArgs s[kMaxBatch];
+  FusedAppend app;
 };
 
 // Query rows per workgroup: the 16-bit kernel (4 wavefronts x 64) and the

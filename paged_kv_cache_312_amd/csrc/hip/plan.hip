@@ -51,7 +51,9 @@ __global__ void rowtab_kernel(RowtabArgs a) {
     a.n_pos = a.desc->n_tiles * 64;
   }
   if (j >= a.n_pos) return;
-  a.rowtab[j] = row_code(a, j < a.kv_len ? j : 0);
+  // with no key from the tables (every key of the step the frame's own), the
+  // padding positions take row 0 of patch page 0
+  a.rowtab[j] = a.kv_len > 0 ? row_code(a, j < a.kv_len ? j : 0) : 0u;
 }
 
 }  // namespace

@@ -113,13 +113,17 @@ def run_stream(cfg: workloads.StreamConfig, check_steps: Optional[Iterable[int]]
                blocks: Optional[Sequence[int]] = None, num_splits: int = 0,
                deferred: bool = False, accept: Optional[List[bool]] = None,
                dump_every: int = 1, q_scale: float = 1.0, run_every_step: bool = False,
-               skip_steps: Iterable[int] = (), label: str = "") -> dict:
+               skip_steps: Iterable[int] = (), fused_steps: Iterable[int] = (),
+               label: str = "") -> dict:
     """Drive the whole schedule of ``cfg`` through the library; check the
     bookkeeping against the reference allocator and, at the checked steps, the
     attention outputs against the oracle.  Steps in ``skip_steps`` (single
     frames) are skip-append frames: planned and run with the frame's own rows,
-    never appended; the bookkeeping must not move.  Returns error statistics."""
+    never appended; the bookkeeping must not move.  Steps in ``fused_steps``
+    go through lbm_append_run (append, plan, evict and attention of each block
+    in one call and one launch).  Returns error statistics."""
     skip = set(skip_steps)
+    fused = set(fused_steps)
     sched = workloads.step_schedule(cfg)
     accept = accept or [True] * len(sched)
     check = set(range(len(sched))) if check_steps is None else set(check_steps)
@@ -170,10 +174,22 @@ def run_stream(cfg: workloads.StreamConfig, check_steps: Optional[Iterable[int]]
                     f"max_abs={worst['max_abs']:.3e} rel_l2={worst['rel_l2']:.3e}")
             continue
         before = ref.dump() if not accept[s] else None
-        # protocol: append(0), [evict], plan, run(0), then append(b), run(b)
+        # protocol: append(0), [evict], plan, run(0), then append(b), run(b);
+        # fused: append_run(b) for every block (block 0 reserves, plans, evicts)
         outs = {}
         for b in range(cfg.num_blocks):
             q, k, v = step_in[b]
+            if s in fused:
+                assert accept[s] and not deferred
+                if b == 0:
+                    ref.append(nf)
+                    ref.evict()
+                o = cache.append_run(b, q, k, v)
+                if b == 0:
+                    worst["splits"].add(cache.num_splits())
+                if b in blocks:
+                    outs[b] = o
+                continue
             cache.append_frame(b, k, v)
             if b == 0:
                 ref.append(nf)
