@@ -88,7 +88,8 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic__attn_d64_kernel_bf16__
 KERNEL_SOURCES = ["paged_kv_cache_312_amd/csrc/hip/attn16.hip",
                   "paged_kv_cache_312_amd/csrc/hip/attn_common.h",
                   "paged_kv_cache_312_amd/csrc/hip/merge.hip",
-                  "paged_kv_cache_312_amd/csrc/hip/kernels.h"]
+                  "paged_kv_cache_312_amd/csrc/hip/kernels.h",
+                  "paged_kv_cache_312_amd/csrc/hip/api.hip"]
 APPEND_SOURCES = ["paged_kv_cache_312_amd/csrc/hip/append.hip",
                   "paged_kv_cache_312_amd/csrc/hip/kernels.h"]
 COPY_BYTES = 1 << 30
@@ -168,13 +169,16 @@ def pmc_summary(fetch_dir, write_dir):
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = load(d, counter)
         ids = sorted(per)
-        # steady state only: the two timed steps and the append-timing step
-        # (72 launches at F = 73..75); earlier ones are the first step and
-        # the fill steps, at other shapes
-        attn = [per[i][1] for i in ids if bf16_kernel(per[i][0], "attn_d64_kernel")][-72:]
-        merge = [per[i][1] for i in ids if bf16_kernel(per[i][0], "merge_kernel")][-72:]
-        # the single-frame appends of the same three steps
-        app = [per[i][1] for i in ids if "append_scatter_kernel" in per[i][0]][-72:]
+        # steady state only: the two timed steps (48 fused launches at F =
+        # 73, 74), not the append-timing step after them (24 launches without
+        # the append) nor the first step and the fill steps (other shapes)
+        # (the counter runs time bf16 only, so every attention instance is a
+        # bf16 one; rocprofv3 may print the skip-append form's name without
+        # its template arguments)
+        attn = [per[i][1] for i in ids if "attn_d64_kernel" in per[i][0]][-72:-24]
+        merge = [per[i][1] for i in ids if bf16_kernel(per[i][0], "merge_kernel")][-72:-24]
+        # the separate single-frame appends of the append-timing step
+        app = [per[i][1] for i in ids if "append_scatter_kernel" in per[i][0]][-23:]
         copy = [per[i][1] for i in ids if "elementwise" in per[i][0]][-3:]
         if not attn or len(copy) < 3:
             raise SystemExit(f"{counter}: attention or calibration dispatches missing")
@@ -201,8 +205,8 @@ def pmc_summary(fetch_dir, write_dir):
                    append_fetch_bytes=round(a_fetch), append_write_bytes=round(a_write))
     os.makedirs(os.path.dirname(TRAFFIC_RECORD), exist_ok=True)
     with open(TRAFFIC_RECORD, "w") as fh:
-        fh.write("HBM traffic of one lbm_run (attention + merge) and of one single-frame "
-                 "append, 24-block ViT-L step; written by "
+        fh.write("HBM traffic of one lbm_append_run (attention with the block's append, + "
+                 "merge) and of one separate single-frame append, 24-block ViT-L step; written by "
                  "'bench.py --pmc-summary' from two rocprofv3 --pmc runs of 'bench.py --steps 2 "
                  "--warmup 0 --no-cpu-baseline --no-variants --no-windows --calibrate-copy' (FETCH_SIZE, "
                  "then WRITE_SIZE)\n")

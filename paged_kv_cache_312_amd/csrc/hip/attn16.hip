@@ -14,13 +14,14 @@
 // and the conversions.
 //
 // Structure (D = 64):
-//  * a workgroup = 4 wavefronts = 256 query rows of one head over one key
-//    range (split); each wavefront owns 64 rows as two halves of 32, so every
-//    K and V operand read from LDS feeds two MFMAs.  A wavefront whose rows
-//    all lie past the step's queries only loads its share of each tile and
-//    keeps the barriers, so the step's last query group proceeds in step with
-//    the groups that share its key range (and its tiles in L2); one whose
-//    second half lies past them computes its first half only;
+//  * a workgroup = 4 wavefronts = up to 256 query rows of one head over one
+//    key range (split); each wavefront owns up to 64 rows as two halves of
+//    32, so every K and V operand read from LDS feeds two MFMAs.  The step's
+//    32-row halves are dealt evenly to the query groups (1375 rows: 8 halves
+//    in the first group, 7 in the other five), so the groups that share a
+//    key range do equal work and stay in step on its tiles in L2.  A
+//    wavefront with one half computes that half only; one without rows only
+//    loads its share of each tile and keeps the barriers;
 //  * 64-key tiles of K and V go from HBM straight into LDS (row-major, global
 //    loads with an LDS destination, no staging registers) through rings of
 //    four stages each, three tiles ahead of use; one barrier per tile;
@@ -226,9 +227,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   const int32_t HD = a.H * D;
   const int32_t t_begin = split * a.tiles_per_split;
   const int32_t t_end = min(a.n_tiles, t_begin + a.tiles_per_split);
-  // Rows: wavefront w owns rows 64w .. 64w+63 of the group's 256, as two
-  // halves of 32; this lane's row in half h is qrow0 + 32h.
-  const int32_t w_row0 = qt * kRowsPerWG16 + wave * 64;
+  // Rows: the step's ceil(Tq / 32) halves of 32 rows are dealt to the n_qt
+  // query groups as evenly as whole halves allow (base or base + 1 each, the
+  // larger groups first), so that the groups sharing a key range do equal
+  // work and stay in step on its tiles; wavefront w takes halves 2w and
+  // 2w + 1 of its group while the group has them (nh of them: 2, 1 or 0).
+  // This lane's row in half h is qrow0 + 32h.
+  const int32_t n_half = (a.Tq + 31) / 32;
+  const int32_t base = n_half / a.n_qt, rem = n_half - base * a.n_qt;
+  const int32_t g_halves = base + (qt < rem ? 1 : 0);
+  const int32_t nh = __builtin_amdgcn_readfirstlane(min(max(g_halves - 2 * wave, 0), 2));
+  const int32_t w_row0 = 32 * (base * qt + min(qt, rem) + 2 * wave);
   const int32_t qrow0 = w_row0 + l32;
   if (t_end <= t_begin) {
     // a split left without keys (graph-replayed steps keep the capture's split
@@ -236,7 +245,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int32_t qrow = qrow0 + 32 * h;
-      if (qrow < a.Tq) {
+      if (h < nh && qrow < a.Tq) {
         const size_t rh = (size_t(split) * a.rows_pad + qrow) * a.H + head;
         float* po = a.part_o + rh * D;
 #pragma unroll
@@ -249,10 +258,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     }
     return;
   }
-  // a wavefront whose rows are all past the step's queries only loads its
-  // share of every tile and keeps the workgroup's barriers (the last query
-  // group's wavefronts beyond its rows)
-  const bool idle = w_row0 >= a.Tq;
+  // a wavefront without rows (a group of fewer than 7 halves, at small Tq)
+  // only loads its share of every tile and keeps the workgroup's barriers
+  const bool idle = nh == 0;
 
   // Q as the B operand of S^T = K Q^T: half h's row, columns 16ks + 8hh ..
   // +7, pre-multiplied by log2(e)/sqrt(D) (rounded to T) so that the MFMA
@@ -262,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int32_t qrow = qrow0 + 32 * h;
-    if (qrow < a.Tq) {
+    if (h < nh && qrow < a.Tq) {
       const h8* qp = reinterpret_cast<const h8*>(
           reinterpret_cast<const uint16_t*>(a.q) + size_t(qrow) * HD + head * D + 8 * hh);
 #pragma unroll
@@ -692,8 +700,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     LBM_WAIT_VMCNT(0);
     return;
   }
-  // NH halves hold rows: a wavefront whose second half lies past the step's
-  // queries (in the last query group) runs the first half only
+  // NH halves hold rows: a wavefront with one half runs that half only
   auto steps = [&](auto nh_c) __attribute__((always_inline)) {
     if (n_t == 1) {
       tile(nh_c, 0, true, true, 0);
@@ -727,7 +734,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     }
     tile(nh_c, n_t - 1, false, true, (n_t - 1) & (NST - 1));
   };
-  if (w_row0 + 32 >= a.Tq)
+  if (nh == 1)
     steps(std::integral_constant<int, 1>{});
   else
     steps(std::integral_constant<int, 2>{});
@@ -738,7 +745,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int32_t qrow = qrow0 + 32 * h;
-    if (qrow >= a.Tq) continue;
+    if (h >= nh || qrow >= a.Tq) continue;
     const float l_tot = l_run[h] + __shfl_xor(l_run[h], 32);
     if (a.num_splits == 1) {
       const float inv = 1.f / l_tot;
