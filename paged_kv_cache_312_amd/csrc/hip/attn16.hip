@@ -52,8 +52,8 @@
 //    row-major tile through gfx950's LDS transpose reads;
 //  * 221-223 VGPRs and no scratch, two workgroups per CU; the steady-state
 //    loop takes four steps per iteration, so LDS operand offsets are constants;
-//  * with several splits, each writes (O, m, l) partials that a separate merge
-//    kernel combines (a kernel boundary orders them: no fences, which on this
+//  * with several splits, each writes its partial (O / l rounded to the input
+//    type, and m, l in fp32) that a separate merge kernel combines (a kernel boundary orders them: no fences, which on this
 //    chip would write back and invalidate the XCD's L2 that the workgroups
 //    share);
 //  * one launch may cover several independent streams (a table of per-stream
@@ -247,12 +247,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
       const int32_t qrow = qrow0 + 32 * h;
       if (h < nh && qrow < a.Tq) {
         const size_t rh = (size_t(split) * a.rows_pad + qrow) * a.H + head;
-        float* po = a.part_o + rh * D;
+        T* po = reinterpret_cast<T*>(a.part_o) + rh * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<float4*>(po + db * 32 + 8 * i + 4 * hh) = make_float4(0.f, 0.f, 0.f, 0.f);
+            *reinterpret_cast<uint2*>(po + db * 32 + 8 * i + 4 * hh) = make_uint2(0u, 0u);
         if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + rh * 2) = make_float2(-INFINITY, 0.f);
       }
     }
@@ -747,31 +747,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     const int32_t qrow = qrow0 + 32 * h;
     if (h >= nh || qrow >= a.Tq) continue;
     const float l_tot = l_run[h] + __shfl_xor(l_run[h], 32);
-    if (a.num_splits == 1) {
-      const float inv = 1.f / l_tot;
-      T* op = reinterpret_cast<T*>(a.out) + size_t(qrow) * HD + head * D;
+    // the output (one split), or the split's normalised partial O / l in T
+    // beside its (m, l) in fp32 (several splits; the merge weighs each by l)
+    const float inv = 1.f / l_tot;
+    const size_t rh = (size_t(split) * a.rows_pad + qrow) * a.H + head;
+    T* op = a.num_splits == 1
+                ? reinterpret_cast<T*>(a.out) + size_t(qrow) * HD + head * D
+                : reinterpret_cast<T*>(a.part_o) + rh * D;
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          typedef T h4 __attribute__((ext_vector_type(4)));
-          h4 w;
+      for (int i = 0; i < 4; ++i) {
+        typedef T h4 __attribute__((ext_vector_type(4)));
+        h4 w;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) w[j] = static_cast<T>(o[h][db][4 * i + j] * inv);
-          *reinterpret_cast<h4*>(op + db * 32 + 8 * i + 4 * hh) = w;
-        }
-    } else {
-      const size_t rh = (size_t(split) * a.rows_pad + qrow) * a.H + head;
-      float* po = a.part_o + rh * D;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<float4*>(po + db * 32 + 8 * i + 4 * hh) =
-              make_float4(o[h][db][4 * i], o[h][db][4 * i + 1], o[h][db][4 * i + 2],
-                          o[h][db][4 * i + 3]);
-      if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + rh * 2) = make_float2(m_run[h], l_tot);
-    }
+        for (int j = 0; j < 4; ++j) w[j] = static_cast<T>(o[h][db][4 * i + j] * inv);
+        *reinterpret_cast<h4*>(op + db * 32 + 8 * i + 4 * hh) = w;
+      }
+    if (a.num_splits > 1 && hh == 0)
+      *reinterpret_cast<float2*>(a.part_ml + rh * 2) = make_float2(m_run[h], l_tot);
   }
 }
 

@@ -55,7 +55,8 @@ struct AttnArgs {
   const void* patch_pool;     // [pages][2][P][H][D]
   const void* special_pool;   // [pages][2][SPS][H][D]
   const uint32_t* rowtab;     // [n_tiles * 64] row codes (see RowtabArgs)
-  float* part_o;              // [splits][rows_pad][H][D] unnormalised partial outputs
+  float* part_o;              // [splits][rows_pad][H][D] partial outputs: unnormalised fp32 (fp32
+                              // kernel) or O / l in the 16-bit input type (16-bit kernels)
   float* part_ml;             // [splits][rows_pad][H][2] (running max in base-2 units, partial sum)
   int32_t Tq, H;
   int32_t vstride_patch;      // bytes from a K row to its V row: P * H * D * elt

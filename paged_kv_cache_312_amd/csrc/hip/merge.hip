@@ -1,11 +1,14 @@
 // Merge of key-range splits.
 //
 // When one (query group, head) is cut into several key ranges, each range
-// leaves an unnormalised partial output O_s with its running max m_s and sum
-// l_s; the result is out = sum_s w_s O_s / sum_s w_s l_s with
-// w_s = 2^(m_s - M), M = max_s m_s -- the usual combination of online-softmax
-// partials (each O_s and l_s is relative to its own m_s; maxima are kept in
-// base-2 exponent units, i.e. raw scores times log2(e)/sqrt(D)).
+// leaves a partial output O_s with its running max m_s and sum l_s; the
+// result is out = sum_s w_s O_s / sum_s w_s l_s with w_s = 2^(m_s - M),
+// M = max_s m_s -- the usual combination of online-softmax partials (each
+// O_s and l_s is relative to its own m_s; maxima are kept in base-2 exponent
+// units, i.e. raw scores times log2(e)/sqrt(D)).  The fp32 kernel stores O_s
+// unnormalised in fp32; the 16-bit kernels store O_s / l_s rounded to their
+// input type (half the bytes; its range is that of V), which enters here
+// weighted by w_s l_s.
 // Memory-bound: one thread per 4 output columns of one (row, head), which
 // issues the loads of up to eight splits' partials together and then combines
 // them (a loop that loaded one split per iteration would wait out one memory
@@ -15,8 +18,10 @@
 namespace lbm {
 namespace {
 
-template <typename OutT, int D>
+// PartT: float (unnormalised O_s) or the 16-bit input type (O_s / l_s)
+template <typename OutT, typename PartT, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
+  constexpr bool kNorm = sizeof(PartT) == 2;
   constexpr int CPR = D / 4;    // float4 chunks per (row, head)
   constexpr int kBatch = 8;     // splits loaded together
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -37,7 +42,14 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
       const size_t srh = size_t(s0 + j) * split_stride + size_t(rh);
       if (s0 + j < a.num_splits) {
         ml[j] = *reinterpret_cast<const float2*>(a.part_ml + srh * 2);
-        o[j] = *reinterpret_cast<const float4*>(a.part_o + srh * D + chunk * 4);
+        if constexpr (kNorm) {
+          typedef PartT p4 __attribute__((ext_vector_type(4)));
+          const p4 x = *reinterpret_cast<const p4*>(reinterpret_cast<const PartT*>(a.part_o) +
+                                                    srh * D + chunk * 4);
+          o[j] = make_float4(float(x[0]), float(x[1]), float(x[2]), float(x[3]));
+        } else {
+          o[j] = *reinterpret_cast<const float4*>(a.part_o + srh * D + chunk * 4);
+        }
       } else {
         ml[j] = make_float2(-INFINITY, 0.f);
         o[j] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -55,8 +67,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
     acc.w *= r;
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const float w = fast_exp2(ml[j].x - Mb);
-      den += w * ml[j].y;
+      const float wl = fast_exp2(ml[j].x - Mb) * ml[j].y;
+      const float w = kNorm ? wl : fast_exp2(ml[j].x - Mb);
+      den += wl;
       acc.x += w * o[j].x;
       acc.y += w * o[j].y;
       acc.z += w * o[j].z;
@@ -78,13 +91,13 @@ hipError_t launch_merge(const AttnArgs& a, int32_t head_dim, int32_t dtype, hipS
   const int64_t total = int64_t(a.Tq) * a.H * (head_dim / 4);
   const dim3 grid(uint32_t((total + 255) / 256)), block(256);
   if (dtype == LBM_BF16 && head_dim == 64)
-    hipLaunchKernelGGL((merge_kernel<__bf16, 64>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((merge_kernel<__bf16, __bf16, 64>), grid, block, 0, stream, a);
   else if (dtype == LBM_F16 && head_dim == 64)
-    hipLaunchKernelGGL((merge_kernel<_Float16, 64>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((merge_kernel<_Float16, _Float16, 64>), grid, block, 0, stream, a);
   else if (dtype == LBM_F32 && head_dim == 64)
-    hipLaunchKernelGGL((merge_kernel<float, 64>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((merge_kernel<float, float, 64>), grid, block, 0, stream, a);
   else if (dtype == LBM_F32 && head_dim == 32)
-    hipLaunchKernelGGL((merge_kernel<float, 32>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((merge_kernel<float, float, 32>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
