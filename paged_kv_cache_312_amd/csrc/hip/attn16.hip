@@ -446,6 +446,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     }
     unbias(b_c, nh_c, kb, s);
   };
+  // block kb's K operands (4 contraction steps) from stage K
+  auto read_k = [&](const uint16_t* K, int kb, h8* kf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      kf[ks] = *reinterpret_cast<const h8*>(K + k_row + kb * 32 * LS + (((2 * ks + hh) ^ k_x) * 8));
+  };
+  // block 0's score chains from operands read ahead (no bias)
+  auto qk_block_kf = [&](auto nh_c, const h8* kf, f32x16 (*s)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int h = 0; h < decltype(nh_c)::value; ++h)
+        s[h][0] = Elt<T>::mfma(kf[ks], qf[h][ks], ks == 0 ? zero : s[h][0]);
+  };
   // the same with the bias taken at run time (the rare paths)
   auto qk_block_any = [&](auto nh_c, const uint16_t* K, int kb, f32x16 (*s)[2])
                           __attribute__((always_inline)) {
@@ -559,8 +573,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   // block 1 finds block 0's terms already in O, which the rescale carries to
   // the new max).  Any max not below the true one gives the same quotient,
   // since numerator and denominator share it.
-  auto tile = [&](auto nh_c, int32_t i, bool first, bool last, int stage)
-                  __attribute__((always_inline)) {
+  auto tile = [&](auto nh_c, int32_t i, bool first, bool last, int stage,
+                  const h8* kf0 = nullptr) __attribute__((always_inline)) {
     constexpr int NH = decltype(nh_c)::value;
     const uint16_t* K = lds_k[stage];
     const uint16_t* V = lds_v[stage];
@@ -569,7 +583,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     float lt0[2], lt1[2];
     // scores against a running max of 0 (the rare path below corrects a
     // biased wavefront's)
-    qk_block(std::false_type{}, nh_c, K, 0, s);
+    if (kf0)
+      qk_block_kf(nh_c, kf0, s);
+    else
+      qk_block(std::false_type{}, nh_c, K, 0, s);
     if (last) mask_block(nh_c, i, 0, s);
     if (first) {
       // the split's first tile (the running max is 0 here)
@@ -713,18 +730,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     // mod 4 at the top) is a constant and its LDS operand addresses fold into
     // the instructions' offsets
     int32_t i = 1;
+    // each step reads block 0's K operands before issuing its loads, so that
+    // their LDS latency overlaps the load addresses
+    h8 kf0[4];
     for (; i + 4 < n_t; i += 4) {
+      read_k(lds_k[1], 0, kf0);
+      __builtin_amdgcn_sched_barrier(0);
       step_loads(i);
-      tile(nh_c, i, false, false, 1);
+      tile(nh_c, i, false, false, 1, kf0);
       end_step(i);
+      read_k(lds_k[2], 0, kf0);
+      __builtin_amdgcn_sched_barrier(0);
       step_loads(i + 1);
-      tile(nh_c, i + 1, false, false, 2);
+      tile(nh_c, i + 1, false, false, 2, kf0);
       end_step(i + 1);
+      read_k(lds_k[3], 0, kf0);
+      __builtin_amdgcn_sched_barrier(0);
       step_loads(i + 2);
-      tile(nh_c, i + 2, false, false, 3);
+      tile(nh_c, i + 2, false, false, 3, kf0);
       end_step(i + 2);
+      read_k(lds_k[0], 0, kf0);
+      __builtin_amdgcn_sched_barrier(0);
       step_loads(i + 3);
-      tile(nh_c, i + 3, false, false, 0);
+      tile(nh_c, i + 3, false, false, 0, kf0);
       end_step(i + 3);
     }
     for (; i + 1 < n_t; ++i) {
