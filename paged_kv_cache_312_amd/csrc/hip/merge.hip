@@ -9,10 +9,11 @@
 // unnormalised in fp32; the 16-bit kernels store O_s / l_s rounded to their
 // input type (half the bytes; its range is that of V), which enters here
 // weighted by w_s l_s.
-// Memory-bound: one thread per 4 output columns of one (row, head), which
-// issues the loads of up to eight splits' partials together and then combines
-// them (a loop that loaded one split per iteration would wait out one memory
-// latency per split).
+// Memory-bound: one thread per 16 bytes of each partial row (8 columns of a
+// 16-bit partial, 4 of an fp32 one) of one (row, head), which issues the
+// loads of up to eight splits' partials together and then combines them (a
+// loop that loaded one split per iteration would wait out one memory latency
+// per split), and writes its columns with one 16-byte store.
 #include "attn_common.h"
 
 namespace lbm {
@@ -22,37 +23,36 @@ namespace {
 template <typename OutT, typename PartT, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
   constexpr bool kNorm = sizeof(PartT) == 2;
-  constexpr int CPR = D / 4;    // float4 chunks per (row, head)
-  constexpr int kBatch = 8;     // splits loaded together
+  constexpr int CW = 16 / sizeof(PartT);  // columns per thread
+  constexpr int CPR = D / CW;             // threads per (row, head)
+  constexpr int kBatch = 8;               // splits loaded together
+  typedef PartT pvec __attribute__((ext_vector_type(CW)));
+  typedef OutT ovec __attribute__((ext_vector_type(CW)));
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t total = int64_t(a.Tq) * a.H * CPR;
   if (idx >= total) return;
   const int32_t chunk = int32_t(idx % CPR);
   const int64_t rh = idx / CPR;  // (row, head) = row * H + head
   const size_t split_stride = size_t(a.rows_pad) * a.H;
+  const PartT* part = reinterpret_cast<const PartT*>(a.part_o);
   // M: the largest m_s so far; den and acc are relative to it.  A split
   // without keys has m = -inf, l = 0, O = 0 and weighs 0.
   float M = -INFINITY, den = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[CW];
+#pragma unroll
+  for (int c = 0; c < CW; ++c) acc[c] = 0.f;
   for (int32_t s0 = 0; s0 < a.num_splits; s0 += kBatch) {
     float2 ml[kBatch];
-    float4 o[kBatch];
+    pvec o[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const size_t srh = size_t(s0 + j) * split_stride + size_t(rh);
       if (s0 + j < a.num_splits) {
         ml[j] = *reinterpret_cast<const float2*>(a.part_ml + srh * 2);
-        if constexpr (kNorm) {
-          typedef PartT p4 __attribute__((ext_vector_type(4)));
-          const p4 x = *reinterpret_cast<const p4*>(reinterpret_cast<const PartT*>(a.part_o) +
-                                                    srh * D + chunk * 4);
-          o[j] = make_float4(float(x[0]), float(x[1]), float(x[2]), float(x[3]));
-        } else {
-          o[j] = *reinterpret_cast<const float4*>(a.part_o + srh * D + chunk * 4);
-        }
+        o[j] = *reinterpret_cast<const pvec*>(part + srh * D + chunk * CW);
       } else {
         ml[j] = make_float2(-INFINITY, 0.f);
-        o[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        o[j] = pvec(PartT(0));
       }
     }
     float Mb = M;
@@ -61,34 +61,30 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
     if (Mb == -INFINITY) continue;  // no keys in any split so far
     const float r = fast_exp2(M - Mb);  // 0 while M is still -inf
     den *= r;
-    acc.x *= r;
-    acc.y *= r;
-    acc.z *= r;
-    acc.w *= r;
+#pragma unroll
+    for (int c = 0; c < CW; ++c) acc[c] *= r;
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const float wl = fast_exp2(ml[j].x - Mb) * ml[j].y;
       const float w = kNorm ? wl : fast_exp2(ml[j].x - Mb);
       den += wl;
-      acc.x += w * o[j].x;
-      acc.y += w * o[j].y;
-      acc.z += w * o[j].z;
-      acc.w += w * o[j].w;
+#pragma unroll
+      for (int c = 0; c < CW; ++c) acc[c] += w * float(o[j][c]);
     }
     M = Mb;
   }
   const float inv = 1.f / den;
-  OutT* op = reinterpret_cast<OutT*>(a.out) + rh * D + chunk * 4;
-  op[0] = OutT(acc.x * inv);
-  op[1] = OutT(acc.y * inv);
-  op[2] = OutT(acc.z * inv);
-  op[3] = OutT(acc.w * inv);
+  ovec res;
+#pragma unroll
+  for (int c = 0; c < CW; ++c) res[c] = OutT(acc[c] * inv);
+  *reinterpret_cast<ovec*>(reinterpret_cast<OutT*>(a.out) + rh * D + chunk * CW) = res;
 }
 
 }  // namespace
 
 hipError_t launch_merge(const AttnArgs& a, int32_t head_dim, int32_t dtype, hipStream_t stream) {
-  const int64_t total = int64_t(a.Tq) * a.H * (head_dim / 4);
+  const int32_t cw = dtype == LBM_F32 ? 4 : 8;  // columns per thread (16 bytes of partial)
+  const int64_t total = int64_t(a.Tq) * a.H * (head_dim / cw);
   const dim3 grid(uint32_t((total + 255) / 256)), block(256);
   if (dtype == LBM_BF16 && head_dim == 64)
     hipLaunchKernelGGL((merge_kernel<__bf16, __bf16, 64>), grid, block, 0, stream, a);
