@@ -34,14 +34,15 @@
 //  * per-step row table (one code per key position) gives each K/V row's
 //    address, so the loop does no page arithmetic;
 //  * online softmax in fp32 with exp2 and the scale folded into Q, against a
-//    stale running max: 0 unless a row's first max falls outside a window
-//    around 0 (wide for bf16, narrow for fp16) and raised (O rescaled, the
-//    block's scores recomputed from LDS) only when a lane's weights of a key
-//    block would sum past a type-dependent limit.  The common path computes
-//    scores from 0 and takes their exponentials as they are: no subtraction
-//    and no bias work.  A wavefront with some max not 0 ("biased") takes a
-//    slower path on every tile that subtracts the max on the vector ALU and
-//    redoes key block 0.  Row sums by 16-bit dot products of the rounded
+//    stale running max: kBase (4) unless a row's first max falls outside a
+//    window around it (wide for bf16, narrow for fp16) and raised (O
+//    rescaled, the block's scores recomputed from LDS) only when a lane's
+//    weights of a key block would sum past a type-dependent limit.  The
+//    common path starts the score chains at -kBase (an inline constant of
+//    the MFMA) and takes the exponentials of the scores as they are: no
+//    subtraction and no bias work.  A wavefront with some max not kBase
+//    ("biased") takes a slower path on every tile that subtracts the
+//    difference on the vector ALU and redoes key block 0.  Row sums by 16-bit dot products of the rounded
 //    weights;
 //  * each tile in two 32-key blocks, in the order K Q^T (block 0), K Q^T
 //    (block 1) beside block 0's exponentials, P V (block 0) beside block 1's
@@ -76,8 +77,8 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 //  kJump: the largest sum of a lane's 16 weights of one key block before the
 //    running max is raised (keeps every weight, and P in the input type,
 //    finite);
-//  [kZeroLo, kZeroHi]: the window of a row's first max (base-2 units) in
-//    which the running max stays 0.
+//  [kZeroLo, kZeroHi]: the window of a row's first max (base-2 units, less
+//    kBase) in which the running max stays kBase.
 template <typename T> struct Elt;
 template <> struct Elt<__bf16> {
   typedef __bf16 v8 __attribute__((ext_vector_type(8)));
@@ -104,6 +105,15 @@ template <> struct Elt<_Float16> {
   static constexpr float kJump = 0x1p12f;
   static constexpr float kZeroLo = -4.f, kZeroHi = 8.f;
 };
+
+// The running max a row keeps unless its scores call for another (base-2
+// units): the score chains start at -kBase, so the weights 2^(s - kBase) of
+// unit-scale logits lie below 1 and seldom cross it.  Weights on both sides
+// of 1 flip every exponent bit of the P V operand from one to the next; kept
+// below it, the operand's upper exponent bits hold still, and the matrix
+// cores switch less.  A power of two that the MFMA takes as an inline
+// constant (0.5, 1, 2 or 4), so the offset costs no instruction.
+constexpr float kBase = 4.f;
 
 constexpr int D = 64;
 constexpr int LS = 64;              // LDS row = one key's 64 columns, 128 bytes
@@ -409,28 +419,31 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[h][db][e] = 0.f;
-  // per half: running max of the row's scores in base-2 units (0 until the
-  // row needs another, stale between jumps) and this lane's share of the row
-  // sum relative to it
-  float m_run[2] = {0.f, 0.f};
+  // per half: running max of the row's scores in base-2 units (kBase until
+  // the row needs another, stale between jumps) and this lane's share of the
+  // row sum relative to it
+  float m_run[2] = {kBase, kBase};
   float l_run[2] = {0.f, 0.f};
-  // some half's running max is not 0 (wavefront-uniform): every tile then
-  // takes the rare path, which subtracts it from the scores
+  // some half's running max is not kBase (wavefront-uniform): every tile
+  // then takes the rare path, which subtracts the difference from the scores
   int32_t biased = 0;
   const h2 ones = {static_cast<T>(1.0f), static_cast<T>(1.0f)};
-  const f32x16 zero = {};
+  // the score chains' start: -kBase in every element (an inline constant of
+  // the MFMA's accumulator input, so the offset costs no instruction)
+  const f32x16 c_start = {-kBase, -kBase, -kBase, -kBase, -kBase, -kBase, -kBase, -kBase,
+                       -kBase, -kBase, -kBase, -kBase, -kBase, -kBase, -kBase, -kBase};
 
   // S^T[key][row] - m of key block kb (keys 32kb .. 32kb+31) of a tile, for
   // the wavefront's NH halves, in base-2 units: lane holds row l32 (+32h) and
   // keys 32kb + 8j + 4hh + u (element 4j + u of s[h][kb]); each K operand
-  // read feeds every half's MFMA.  Each chain starts from 0; a biased
-  // wavefront then subtracts m_run on the vector ALU.
+  // read feeds every half's MFMA.  Each chain starts from -kBase; a biased
+  // wavefront then subtracts m_run - kBase on the vector ALU.
   auto unbias = [&](auto b_c, auto nh_c, int kb, f32x16 (*s)[2]) __attribute__((always_inline)) {
     if constexpr (decltype(b_c)::value) {
 #pragma unroll
       for (int h = 0; h < decltype(nh_c)::value; ++h)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[h][kb][e] -= m_run[h];
+        for (int e = 0; e < 16; ++e) s[h][kb][e] -= m_run[h] - kBase;
     }
   };
   auto qk_block = [&](auto b_c, auto nh_c, const uint16_t* K, int kb, f32x16 (*s)[2])
@@ -442,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
                                                  (((2 * ks + hh) ^ k_x) * 8));
 #pragma unroll
       for (int h = 0; h < NH; ++h)
-        s[h][kb] = Elt<T>::mfma(kf, qf[h][ks], ks == 0 ? zero : s[h][kb]);
+        s[h][kb] = Elt<T>::mfma(kf, qf[h][ks], ks == 0 ? c_start : s[h][kb]);
     }
     unbias(b_c, nh_c, kb, s);
   };
@@ -458,7 +471,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int h = 0; h < decltype(nh_c)::value; ++h)
-        s[h][0] = Elt<T>::mfma(kf[ks], qf[h][ks], ks == 0 ? zero : s[h][0]);
+        s[h][0] = Elt<T>::mfma(kf[ks], qf[h][ks], ks == 0 ? c_start : s[h][0]);
   };
   // the same with the bias taken at run time (the rare paths)
   auto qk_block_any = [&](auto nh_c, const uint16_t* K, int kb, f32x16 (*s)[2])
@@ -564,8 +577,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   // weights; P V of block 0 beside block 1's weights; P V of block 1.
   // Softmax runs against the running max as it stands (the scores arrive
   // with it subtracted).  On the split's first tile a row whose max lies
-  // outside [kZeroLo, kZeroHi] takes that max (so the largest weight is 1
-  // and the row sum never underflows); others keep 0.  Afterwards the max is
+  // outside [kZeroLo, kZeroHi] of kBase takes that max (so the largest
+  // weight is 1 and the row sum never underflows); others keep kBase.
+  // Afterwards the max is
   // raised only when some lane's weights of a block would sum past kJump (a
   // jump of the max): then the block's scores are recomputed from the stage
   // (resident until the step's barrier), O and l rescaled and the block's
@@ -581,7 +595,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     f32x16 s[2][2];
     u32x4 pb[2][4];
     float lt0[2], lt1[2];
-    // scores against a running max of 0 (the rare path below corrects a
+    // scores against a running max of kBase (the rare path below corrects a
     // biased wavefront's)
     if (kf0)
       qk_block_kf(nh_c, kf0, s);
@@ -589,7 +603,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
       qk_block(std::false_type{}, nh_c, K, 0, s);
     if (last) mask_block(nh_c, i, 0, s);
     if (first) {
-      // the split's first tile (the running max is 0 here)
+      // the split's first tile (the running max is kBase here)
       qk_block(std::false_type{}, nh_c, K, 1, s);
       if (last) mask_block(nh_c, i, 1, s);
       float r[2];
@@ -603,11 +617,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
       }
       if (__ballot(any)) {
 #pragma unroll
-        for (int h = 0; h < NH; ++h) m_run[h] = out[h] ? round_up_to<T>(r[h]) : 0.f;
+        for (int h = 0; h < NH; ++h) m_run[h] = out[h] ? round_up_to<T>(r[h] + kBase) : kBase;
         biased = 1;
       }
-      exp_block(nh_c, s, 0, m_run, pb, lt0);
-      exp_block(nh_c, s, 1, m_run, pb, lt1);
+      float sh[2];
+#pragma unroll
+      for (int h = 0; h < NH; ++h) sh[h] = m_run[h] - kBase;
+      exp_block(nh_c, s, 0, sh, pb, lt0);
+      exp_block(nh_c, s, 1, sh, pb, lt1);
 #pragma unroll
       for (int h = 0; h < NH; ++h) l_run[h] += lt0[h] + lt1[h];
       pv_block(nh_c, V, 0, pb);
@@ -626,7 +643,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
 #pragma unroll
     for (int st = 0; st < 4 * NH; ++st) {
       const int ks = st / NH, h = st % NH;
-      s[h][1] = Elt<T>::mfma(kf1[ks], qf[h][ks], ks == 0 ? zero : s[h][1]);
+      s[h][1] = Elt<T>::mfma(kf1[ks], qf[h][ks], ks == 0 ? c_start : s[h][1]);
       exp_part(s, st >> 2, 0, st & 3, pb, lt0);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -642,7 +659,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
 #pragma unroll
       for (int h = 0; h < NH; ++h)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[h][1][e] -= m_run[h];
+        for (int e = 0; e < 16; ++e) s[h][1][e] -= m_run[h] - kBase;
       qk_block_any(nh_c, K, 0, s);
       if (last) mask_block(nh_c, i, 0, s);
       float su[2];
