@@ -625,14 +625,15 @@ def main():
                      "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(),
                      "kernel": "attn_d64_kernel<__bf16> (+ merge_kernel): one lbm_append_run "
-                               "(attention with the block's append carried by extra workgroups)",
+                               "(attention whose query group 0 also stores the block's frame "
+                               "rows it stages into their pages)",
                      "avg_launch_ms": round(avg_launch_ms, 4),
                      "flops_per_launch_avg": flops / n_launch},
         # the timed steps carry each block's append inside its attention
         # launch (lbm_append_run); the separate append kernel (lbm_append_frame)
         # is timed on one more step for reference, and the whole step made of
         # separate calls is a variant below
-        "append": {"mode": "fused into the attention launch",
+        "append": {"mode": "stored by the attention launch (query group 0, from the rows it stages)",
                    "separate_kernel": {
                        "bound": "hbm", "achieved": round(append_gbps, 1), "peak": PEAK_HBM_GBPS,
                        "unit": "GB/s", "frac": round(append_gbps / PEAK_HBM_GBPS, 4),

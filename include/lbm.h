@@ -211,11 +211,13 @@ lbm_status lbm_run_transient(lbm_cache* cache, int32_t block_idx, const void* q,
  * device [num_q_tokens, H, D] as for lbm_run.  block_idx 0 opens the step: it
  * reserves the pages (as lbm_append_frame), plans (num_q_tokens queries), and
  * evicts (as lbm_evict_frames; the ids are not reported).  Every block's call
- * then enqueues one attention launch whose extra workgroups copy the block's
- * rows into the reserved pages while its attention reads the step's own rows
- * from k, v (as lbm_run_transient does) and the rest of the visible set from
- * the pages; the result is the same attention as lbm_append_frame + lbm_plan
- * + lbm_run (the keys taken in another order).  Blocks 1..num_blocks-1 follow
+ * then enqueues one attention launch that reads the step's own rows from k, v
+ * (as lbm_run_transient does) and the rest of the visible set from the pages,
+ * and stores the own rows into the reserved pages: in the 16-bit kernels the
+ * workgroups of query group 0 store the rows they stage, from LDS; the fp32
+ * kernel's launch carries extra workgroups that copy them.  The result is the
+ * same attention as lbm_append_frame + lbm_plan + lbm_run (the keys taken in
+ * another order).  Blocks 1..num_blocks-1 follow
  * block 0 in the same step, each once, with the same num_frames and
  * num_q_tokens.  k and v must stay unchanged until the launch has run.
  * Requires num_frames <= sliding_window (every frame of the step stays

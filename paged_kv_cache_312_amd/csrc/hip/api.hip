@@ -145,9 +145,11 @@ lbm_status copy_record(const std::vector<int32_t>& v, int32_t* buf, int64_t cap,
 // `rowtab`, then the attention launch; both on stream `st`.
 // Positions past kv_len (up to the tile boundary of kv_len + own, the own
 // rows of a skip-append step included) get position 0's code.
+// fused_nf > 0: the plan of lbm_append_run, whose own rows (the last `own`
+// positions) get their destinations as codes.
 lbm_status launch_rowtab_for(const lbm_config& c, const int32_t* pids, const int32_t* sids,
                              int32_t patch_tokens, int32_t kv_len, int32_t own,
-                             uint32_t* rowtab, hipStream_t st) {
+                             uint32_t* rowtab, hipStream_t st, int32_t fused_nf = 0) {
   RowtabArgs r;
   std::memset(&r, 0, sizeof(r));
   r.patch_ids = pids;
@@ -161,6 +163,12 @@ lbm_status launch_rowtab_for(const lbm_config& c, const int32_t* pids, const int
   r.row_bytes = int32_t(size_t(c.num_heads) * c.head_dim * dtype_size(c.dtype));
   r.inv_P = 1.0f / float(r.P);
   r.inv_SPS = 1.0f / float(r.SPS);
+  if (fused_nf > 0) {
+    r.own_rows = own;
+    r.own_S = c.special_per_frame;
+    r.own_T = c.patches_per_frame + c.special_per_frame;
+    r.inv_T = 1.0f / float(r.own_T);
+  }
   const hipError_t e = launch_rowtab(r, st);
   if (e != hipSuccess) return hip_fail(e, "row table launch");
   return LBM_OK;
@@ -590,7 +598,7 @@ lbm_status plan_impl(lbm_cache* c, int32_t num_q_tokens, int32_t own, void* hip_
   lbm_status rs = launch_rowtab_for(
       c->cfg, reinterpret_cast<const int32_t*>(c->workspace + c->ws.patch_ids_off),
       reinterpret_cast<const int32_t*>(c->workspace + c->ws.special_ids_off), p.patch_tokens,
-      p.kv_len, own, reinterpret_cast<uint32_t*>(c->workspace + c->ws.rowtab_off), s);
+      p.kv_len, own, reinterpret_cast<uint32_t*>(c->workspace + c->ws.rowtab_off), s, fused_nf);
   if (rs != LBM_OK) return rs;
 
   const int32_t cap = split_capacity(c->ws, num_q_tokens);
@@ -779,8 +787,15 @@ lbm_status lbm_append_run(lbm_cache* c, int32_t block_idx, const void* q, const 
   f.S = c->cfg.special_per_frame;
   f.SPS = c->cfg.special_page_size;
   f.rc = int32_t(size_t(c->cfg.num_heads) * c->cfg.head_dim * dtype_size(c->cfg.dtype) / 16);
-  // about 16 rows of K or V per workgroup, at most 256 workgroups
-  f.wgs = std::max(1, std::min(256, (2 * f.rows + 15) / 16));
+  if (c->cfg.dtype == LBM_F32) {
+    // the fp32 kernel: extra workgroups copy the rows, about 16 rows of K or
+    // V per workgroup, at most 256 workgroups
+    f.wgs = std::max(1, std::min(256, (2 * f.rows + 15) / 16));
+  } else {
+    // the 16-bit kernels: query group 0 of each key range stores the rows it
+    // stages (their destinations are the row table's own codes)
+    a.own_store = 1;
+  }
   st = launch_attention(c->cfg, &a, c->plan_splits, s, &f);
   if (st != LBM_OK) return st;
   c->appended[size_t(block_idx)] = 1;

@@ -38,8 +38,8 @@
 //    window around it (wide for bf16, narrow for fp16) and raised (O
 //    rescaled, the block's scores recomputed from LDS) only when a lane's
 //    weights of a key block would sum past a type-dependent limit.  The
-//    common path starts the score chains at -kBase (an inline constant of
-//    the MFMA) and takes the exponentials of the scores as they are: no
+//    common path starts the score chains at -kBase (the MFMAs' accumulator
+//    input) and takes the exponentials of the scores as they are: no
 //    subtraction and no bias work.  A wavefront with some max not kBase
 //    ("biased") takes a slower path on every tile that subtracts the
 //    difference on the vector ALU and redoes key block 0.  Row sums by 16-bit dot products of the rounded
@@ -111,8 +111,8 @@ template <> struct Elt<_Float16> {
 // unit-scale logits lie below 1 and seldom cross it.  Weights on both sides
 // of 1 flip every exponent bit of the P V operand from one to the next; kept
 // below it, the operand's upper exponent bits hold still, and the matrix
-// cores switch less.  A power of two that the MFMA takes as an inline
-// constant (0.5, 1, 2 or 4), so the offset costs no instruction.
+// cores switch less.  The chains take it as their accumulator input, so the
+// offset costs no instruction.
 constexpr float kBase = 4.f;
 
 constexpr int D = 64;
@@ -223,11 +223,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     a.tr_start = a.kv_len;
   }
   // item -> (query group, head, key range); the groups sharing a key range
-  // are consecutive items, so they run side by side on one L2
+  // are consecutive items, so they run side by side on one L2.  A head's
+  // key ranges go out last first: the last range holds the frame's own rows,
+  // whose query group 0 stores them in a fused step, and dispatched early its
+  // workgroups have slack (a slot whose first workgroup ends late takes no
+  // second one).
   const int32_t qt = item % a.n_qt;
   const int32_t grp = item / a.n_qt;
   const int32_t head = grp / a.num_splits;
-  const int32_t split = grp - head * a.num_splits;
+  const int32_t split = a.num_splits - 1 - (grp - head * a.num_splits);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -397,6 +401,41 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     code_nx = codes_of(i + 1 + kLead);
     barrier();
   };
+  // lbm_append_run: the workgroups of query group 0 store the frame's own
+  // rows of their tiles (staged in LDS from the caller's rows) into the
+  // pages the step reserved, whose codes the row table holds at the own
+  // positions; the other groups only read them.  At the start of step i,
+  // while position i's stage is resident: wavefront w stores rows 16w ..
+  // 16w+15 of the tile, lane l row 16w + l/4, chunks 2(l%4) and 2(l%4)+1 of
+  // this head's K and V.  The stores count in the vector-memory counter
+  // beside the loads; loads still complete in order, so each step's wait for
+  // its oldest loads stays sufficient.
+  const bool own_store = TR && a.own_store != 0 && qt == 0;
+  // the steps whose tiles hold own rows: [own_i0, own_i1), empty without
+  const int32_t own_i0 = a.tr_start / 64 - t_begin;
+  const int32_t own_i1 = own_store ? (a.kv_len + 63) / 64 - t_begin : own_i0;
+  auto own_write = [&](int32_t i, int stage) __attribute__((always_inline)) {
+    if (!TR || i < own_i0 || i >= own_i1) return;
+    const int r = 16 * wave + (lane >> 2);
+    const int32_t key = (t_begin + i) * 64 + r;
+    if (key < a.tr_start || key >= a.kv_len) return;
+    const uint32_t code = lds_code[i & (NCODE - 1)][r];
+    const bool special = (code >> 31) != 0;
+    char* kd = static_cast<char*>(const_cast<void*>(special ? a.special_pool : a.patch_pool)) +
+               (code & 0x7fffffffu) + head * D * 2;
+    char* vd = kd + (special ? a.vstride_special : a.vstride_patch);
+    const int c0 = 2 * (lane & 3);
+    const uint16_t* kr = &lds_k[stage][r * LS];
+    const uint16_t* vr = &lds_v[stage][r * LS];
+    const uint4 k0 = *reinterpret_cast<const uint4*>(kr + ((c0 ^ k_swz(r)) * 8));
+    const uint4 k1 = *reinterpret_cast<const uint4*>(kr + (((c0 + 1) ^ k_swz(r)) * 8));
+    const uint4 v0 = *reinterpret_cast<const uint4*>(vr + ((c0 ^ v_swz(r)) * 8));
+    const uint4 v1 = *reinterpret_cast<const uint4*>(vr + (((c0 + 1) ^ v_swz(r)) * 8));
+    reinterpret_cast<uint4*>(kd)[c0] = k0;
+    reinterpret_cast<uint4*>(kd)[c0 + 1] = k1;
+    reinterpret_cast<uint4*>(vd)[c0] = v0;
+    reinterpret_cast<uint4*>(vd)[c0 + 1] = v1;
+  };
 
   // K operand: row kb*32 + l32, chunk 2ks + hh (swizzle depends on l32 only).
   // V transpose read: within each 16-lane group g, lane s points at row
@@ -428,10 +467,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   // then takes the rare path, which subtracts the difference from the scores
   int32_t biased = 0;
   const h2 ones = {static_cast<T>(1.0f), static_cast<T>(1.0f)};
-  // the score chains' start: -kBase in every element (an inline constant of
-  // the MFMA's accumulator input, so the offset costs no instruction)
-  const f32x16 c_start = {-kBase, -kBase, -kBase, -kBase, -kBase, -kBase, -kBase, -kBase,
-                       -kBase, -kBase, -kBase, -kBase, -kBase, -kBase, -kBase, -kBase};
+  // the score chains' start: -kBase in every element, held in 16 VGPRs for
+  // the whole kernel (the empty asm makes it a register value: as a constant
+  // shared by a step's four chain starts the compiler would keep it in 16
+  // scalar registers and copy it with eight 64-bit moves per step)
+  f32x16 c_start = {-kBase, -kBase, -kBase, -kBase, -kBase, -kBase, -kBase, -kBase,
+                    -kBase, -kBase, -kBase, -kBase, -kBase, -kBase, -kBase, -kBase};
+  asm volatile("" : "+v"(c_start));
 
   // S^T[key][row] - m of key block kb (keys 32kb .. 32kb+31) of a tile, for
   // the wavefront's NH halves, in base-2 units: lane holds row l32 (+32h) and
@@ -728,18 +770,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   // after each step but the last.
   if (idle) {
     for (int32_t i = 0; i + 1 < n_t; ++i) {
+      own_write(i, i & (NST - 1));
       step_loads(i);
       end_step(i);
     }
+    own_write(n_t - 1, (n_t - 1) & (NST - 1));
     LBM_WAIT_VMCNT(0);
     return;
   }
   // NH halves hold rows: a wavefront with one half runs that half only
   auto steps = [&](auto nh_c) __attribute__((always_inline)) {
     if (n_t == 1) {
+      own_write(0, 0);
       tile(nh_c, 0, true, true, 0);
       return;
     }
+    own_write(0, 0);
     step_loads(0);
     tile(nh_c, 0, true, false, 0);
     end_step(0);
@@ -748,9 +794,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     // the instructions' offsets
     int32_t i = 1;
     // each step reads block 0's K operands before issuing its loads, so that
-    // their LDS latency overlaps the load addresses
+    // their LDS latency overlaps the load addresses.  Tiles with own rows to
+    // store go to the loop below.
+    const int32_t n_fast = min(n_t, own_i0 < own_i1 ? own_i0 + 1 : n_t);
     h8 kf0[4];
-    for (; i + 4 < n_t; i += 4) {
+    for (; i + 4 < n_fast; i += 4) {
       read_k(lds_k[1], 0, kf0);
       __builtin_amdgcn_sched_barrier(0);
       step_loads(i);
@@ -773,10 +821,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
       end_step(i + 3);
     }
     for (; i + 1 < n_t; ++i) {
+      own_write(i, i & (NST - 1));
       step_loads(i);
       tile(nh_c, i, false, false, i & (NST - 1));
       end_step(i);
     }
+    own_write(n_t - 1, (n_t - 1) & (NST - 1));
     tile(nh_c, n_t - 1, false, true, (n_t - 1) & (NST - 1));
   };
   if (nh == 1)

@@ -44,6 +44,13 @@ struct RowtabArgs {
   float inv_P, inv_SPS;
   const StepDesc* desc;       // graph-replayed step: kv_len, patch_tokens from here (the
                               // grid covers the table's capacity)
+  // Plan of lbm_append_run: positions [kv_len, kv_len + own_rows) are the
+  // step's own rows (frame-major, own_T = P + own_S tokens a frame), which the
+  // run reads from the caller's rows; their codes are the rows' destinations
+  // in the pools, the last frames' patch pages of the table and the last
+  // special tokens of the special stream.  0 otherwise.
+  int32_t own_rows, own_T, own_S;
+  float inv_T;
 };
 
 hipError_t launch_rowtab(const RowtabArgs& a, hipStream_t stream);
@@ -69,6 +76,10 @@ struct AttnArgs {
   const void* tv;
   int32_t tr_start;
   int32_t row_bytes;          // H * D * element size
+  // lbm_append_run (16-bit kernels): the workgroups of query group 0 also
+  // store the own rows they stage, from LDS into the rows' pages, whose
+  // codes the row table holds at positions [tr_start, kv_len).
+  int32_t own_store;
   // Graph-replayed step: kv_len, n_tiles and tiles_per_split come from here
   // (num_splits stays the capture's; splits left without keys write empty
   // partials).

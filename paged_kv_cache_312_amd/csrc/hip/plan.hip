@@ -43,6 +43,22 @@ __device__ __forceinline__ uint32_t row_code(const RowtabArgs& a, int32_t j) {
   return uint32_t(row * a.row_bytes) | 0x80000000u;
 }
 
+// Destination code of own row r of a fused step: frame r / T, token r mod T,
+// a patch token of the frame's page (the table's pages after the visible
+// ones) or a special token of the stream after the visible ones.
+__device__ __forceinline__ uint32_t own_code(const RowtabArgs& a, int32_t r) {
+  int32_t fr, t;
+  divmod_small(r, a.own_T, a.inv_T, fr, t);
+  if (t < a.P) {
+    const int64_t row = int64_t(a.patch_ids[a.patch_tokens / a.P + fr]) * 2 * a.P + t;
+    return uint32_t(row * a.row_bytes);
+  }
+  int32_t pi, slot;
+  divmod_small(a.kv_len - a.patch_tokens + fr * a.own_S + (t - a.P), a.SPS, a.inv_SPS, pi, slot);
+  const int64_t row = int64_t(a.special_ids[pi]) * 2 * a.SPS + slot;
+  return uint32_t(row * a.row_bytes) | 0x80000000u;
+}
+
 __global__ void rowtab_kernel(RowtabArgs a) {
   const int32_t j = blockIdx.x * blockDim.x + threadIdx.x;
   if (a.desc) {
@@ -53,7 +69,14 @@ __global__ void rowtab_kernel(RowtabArgs a) {
   if (j >= a.n_pos) return;
   // with no key from the tables (every key of the step the frame's own), the
   // padding positions take row 0 of patch page 0
-  a.rowtab[j] = a.kv_len > 0 ? row_code(a, j < a.kv_len ? j : 0) : 0u;
+  uint32_t code;
+  if (j < a.kv_len)
+    code = row_code(a, j);
+  else if (j - a.kv_len < a.own_rows)
+    code = own_code(a, j - a.kv_len);
+  else
+    code = a.kv_len > 0 ? row_code(a, 0) : 0u;
+  a.rowtab[j] = code;
 }
 
 }  // namespace

@@ -4,7 +4,8 @@ rule-derived visible set, the step's own rows included) on every output of
 small streams and on sampled rows of the ViT-L-shaped single-block stream; the
 bookkeeping against the reference allocator after every step; the pools by
 reading every visible row back through the table, byte for byte against the
-inputs (the rows the launches' extra workgroups wrote); and the protocol
+inputs (the rows the launches wrote: the fp32 kernel's extra workgroups, the
+16-bit kernels' query group 0 from the tiles it stages); and the protocol
 errors, which leave the cache as it was."""
 import numpy as np
 import pytest
@@ -45,10 +46,17 @@ def test_vitl_single_block_fused():
                fused_steps=range(n), label="vitl fused")
 
 
-@pytest.mark.parametrize("cfg", [workloads.get_config(0), SMALL_BF16], ids=["tiny_f32", "small_bf16"])
+@pytest.mark.parametrize("cfg", [workloads.get_config(0), SMALL_BF16,
+                                 SMALL_BF16.replace(name="small_f16", dtype="f16"),
+                                 SMALL_BF16.replace(name="small_bf16_wide", patches_per_frame=300,
+                                                    num_heads=4)],
+                         ids=["tiny_f32", "small_bf16", "small_f16", "small_bf16_wide"])
 def test_fused_append_gather_back_is_byte_exact(cfg):
     """After each fused step, the rows the table points at are the input rows,
-    byte for byte, in visible order (scale, window, specials)."""
+    byte for byte, in visible order (scale, window, specials): written by the
+    fp32 kernel's extra workgroups, or by the 16-bit kernels' query group 0
+    from the tiles it stages (the wide case: own rows over several tiles and
+    key ranges)."""
     from oracle import rules
     cache, _ = make_cache(cfg)
     T, P = cfg.tokens_per_frame, cfg.patches_per_frame
