@@ -207,11 +207,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[NST][TILE];
   __shared__ __attribute__((aligned(16))) uint32_t lds_code[NCODE][64];
 
-  if (b.app.wgs > 0 && int32_t(blockIdx.x) >= b.app.wg0) {
-    // a workgroup of an append carried by this launch
-    fused_append_wg(b.app, int32_t(blockIdx.x) - b.app.wg0);
-    return;
-  }
   int32_t sid;
   const int32_t item = work_item(b, blockIdx.x, sid);
   if (sid < 0) return;
@@ -869,7 +864,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
 hipError_t launch_attn16(const BatchArgs& b, int32_t head_dim, bool fp16, bool transient,
                          hipStream_t stream) {
   if (head_dim != 64) return hipErrorInvalidValue;
-  const dim3 grid(8 * b.items_per_xcd + b.app.wgs), block(kThreads);
+  // (an append carried by the launch is stored by query group 0, own_store;
+  // the launch takes no extra workgroups)
+  if (b.app.wgs != 0) return hipErrorInvalidValue;
+  const dim3 grid(8 * b.items_per_xcd), block(kThreads);
   if (fp16 && transient)
     hipLaunchKernelGGL((attn_d64_kernel<_Float16, true>), grid, block, 0, stream, b);
   else if (fp16)

@@ -98,11 +98,13 @@ struct AttnArgs {
 // launch's item range, each stream's laid out as a single-stream launch's.
 constexpr int kMaxBatch = 8;
 
-// An append carried by an attention launch: workgroups [wg0, wg0 + wgs) of
-// the grid copy one block's rows of the step into their pages, with the
+// An append carried by an fp32 attention launch: workgroups [wg0, wg0 + wgs)
+// of the grid copy one block's rows of the step into their pages, with the
 // placement of append_scatter_kernel, instead of computing attention.  The
 // launch's attention reads those rows from k / v (the skip-append address
-// form), so no workgroup reads a row that another one writes.  wgs = 0: none.
+// form), so no workgroup reads a row that another one writes.  wgs = 0: none
+// (the 16-bit kernels store the rows from the tiles they stage instead:
+// AttnArgs::own_store).
 struct FusedAppend {
   const uint4* k;             // [rows][rc]
   const uint4* v;
