@@ -416,6 +416,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     if (key < a.tr_start || key >= a.kv_len) return;
     const uint32_t code = lds_code[i & (NCODE - 1)][r];
     const bool special = (code >> 31) != 0;
+    // the pools are the cache's own device buffers, read-only to every other
+    // launch form; only this store writes through them
     char* kd = static_cast<char*>(const_cast<void*>(special ? a.special_pool : a.patch_pool)) +
                (code & 0x7fffffffu) + head * D * 2;
     char* vd = kd + (special ? a.vstride_special : a.vstride_patch);
