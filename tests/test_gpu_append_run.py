@@ -83,6 +83,49 @@ def test_fused_append_gather_back_is_byte_exact(cfg):
     cache.close()
 
 
+@pytest.mark.parametrize("nq", [1, 33, 300])
+def test_fused_step_with_fewer_queries(nq):
+    """lbm_append_run with fewer query rows than the step has own rows: the
+    workgroups of query group 0 then hold few rows (wavefronts without any
+    take the load-only path) yet still store every own row.  Each output
+    against the oracle's dense softmax over the visible set built from the
+    input rows (own rows included), and the stored rows byte for byte."""
+    from oracle import attention, rules
+    cfg = SMALL_BF16.replace(name="small_bf16_wide", patches_per_frame=300, num_heads=4)
+    cache, _ = make_cache(cfg)
+    T, P = cfg.tokens_per_frame, cfg.patches_per_frame
+    frames = {}
+    F = 0
+    worst = 0.0
+    for s, nf in enumerate(workloads.step_schedule(cfg)):
+        outs = []
+        for b in range(cfg.num_blocks):
+            q, k, v = workloads.gen_step_qkv(cfg, b, s, nf, DEV)
+            qs = q[:nq].contiguous()
+            outs.append((qs, cache.append_run(b, qs, k, v)))
+            for i in range(nf):
+                frames[(b, F + i)] = (k[i * T:(i + 1) * T], v[i * T:(i + 1) * T])
+        F += nf
+        torch.cuda.synchronize()
+        pf = rules.visible_patch_frames(F, cfg.scale_frames, cfg.sliding_window)
+        for b in range(cfg.num_blocks):
+            Ke = torch.cat([frames[(b, f)][0][:P] for f in pf] +
+                           [frames[(b, f)][0][P:] for f in range(F)])
+            Ve = torch.cat([frames[(b, f)][1][:P] for f in pf] +
+                           [frames[(b, f)][1][P:] for f in range(F)])
+            qs, o = outs[b]
+            ref = attention.dense_attention(qs.float().cpu().numpy(), Ke.float().cpu().numpy(),
+                                            Ve.float().cpu().numpy())
+            err = float(np.abs(o.float().cpu().numpy() - ref).max())
+            worst = max(worst, err)
+            assert err < 2e-2, f"step {s} block {b}: max abs {err:.3e}"
+            Kg, Vg = _gather_visible(cache, b)
+            assert torch.equal(Kg.view(torch.int16), Ke.view(torch.int16)), f"step {s} block {b}: K"
+            assert torch.equal(Vg.view(torch.int16), Ve.view(torch.int16)), f"step {s} block {b}: V"
+    say(f"fused, {nq} queries: worst max_abs {worst:.3e}")
+    cache.close()
+
+
 def test_fused_protocol_errors():
     cfg = SMALL_BF16
     cache, _ = make_cache(cfg)
