@@ -14,12 +14,14 @@
 // and the conversions.
 //
 // Structure (D = 64):
-//  * a workgroup = 4 wavefronts = up to 256 query rows of one head over one
-//    key range (split); each wavefront owns up to 64 rows as two halves of
-//    32, so every K and V operand read from LDS feeds two MFMAs.  The step's
-//    32-row halves are dealt evenly to the query groups (1375 rows: 8 halves
-//    in the first group, 7 in the other five), so the groups that share a
-//    key range do equal work and stay in step on its tiles in L2.  A
+//  * a workgroup = 8 wavefronts = up to 512 query rows of one head over one
+//    key range (split), one workgroup per CU (two wavefronts per SIMD); each
+//    wavefront owns up to 64 rows as two halves of 32, so every K and V
+//    operand read from LDS feeds two MFMAs, and each tile loaded into LDS
+//    serves all 512 rows.  The step's 32-row halves are dealt evenly to the
+//    query groups (1375 rows: 15 halves in the first group, 14 in the other
+//    two), so the groups that share a key range do equal work and stay in
+//    step on its tiles in L2.  A
 //    wavefront with one half computes that half only; one without rows only
 //    loads its share of each tile and keeps the barriers;
 //  * 64-key tiles of K and V go from HBM straight into LDS (row-major, global
@@ -51,8 +53,9 @@
 //  * O^T += V^T P^T on the same MFMA with P taken from registers (no LDS trip),
 //    P rounded to the input type (round to nearest even); the V operand comes from the
 //    row-major tile through gfx950's LDS transpose reads;
-//  * 221-223 VGPRs and no scratch, two workgroups per CU; the steady-state
-//    loop takes four steps per iteration, so LDS operand offsets are constants;
+//  * at most 256 VGPRs and no scratch, one workgroup (two wavefronts per
+//    SIMD) per CU; the steady-state loop takes four steps per iteration, so
+//    LDS operand offsets are constants;
 //  * with several splits, each writes its partial (O / l rounded to the input
 //    type, and m, l in fp32) that a separate merge kernel combines (a kernel boundary orders them: no fences, which on this
 //    chip would write back and invalidate the XCD's L2 that the workgroups
@@ -122,8 +125,10 @@ constexpr int NST = 4;              // LDS stages of K and of V
 constexpr int NCODE = 2 * NST;      // LDS slots of row codes (64 per tile)
 constexpr int kLead = NST - 1;      // tiles whose K and V are loaded ahead of use
 // Global loads (all with an LDS destination) each wavefront issues per tile:
-// two K, two V, then one of row codes.
-constexpr int kLoadsKV = 4;
+// one K, one V, then one of row codes.
+constexpr int kWaves = 8;              // wavefronts per workgroup
+constexpr int kThreads16 = 64 * kWaves;
+constexpr int kLoadsKV = 2;
 constexpr int kLoadsPerStep = kLoadsKV + 1;
 // Loads a wavefront may leave outstanding at the end of a step: this step's
 // and, in the first step, the prologue's loads of position kLead-1.
@@ -197,12 +202,12 @@ __device__ __forceinline__ float round_up_to(float x) {
 // one kernel per element type: attn_d64_kernel<__bf16> and attn_d64_kernel<_Float16>;
 // TR: a skip-append step, whose last keys are the frame's own rows
 template <typename T, bool TR>
-__global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b) {
+__global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs b) {
   typedef typename Elt<T>::v8 h8;
   typedef typename Elt<T>::v2 h2;
   // Rings indexed by tile position x (x = 0 is the split's first tile): K
   // and V of tile x in stage x mod NST, its row codes in slot x mod NCODE.
-  // 66 KB, two workgroups per CU.
+  // 66 KB, one workgroup per CU.
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[NST][TILE];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[NST][TILE];
   __shared__ __attribute__((aligned(16))) uint32_t lds_code[NCODE][64];
@@ -296,9 +301,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
 
   // Loads into LDS: a wavefront instruction fills 1 KB = 8 rows of 128 B,
   // lane j writing row j/8, 16-byte slot j%8.  Wavefront w fills rows 8w..8w+7
-  // and 32+8w..32+8w+7 of each tile (keys lp and lp+32 for thread tid,
-  // lp = tid/8), and slot lc of a row receives the row's chunk lc ^ swizzle,
-  // which places the tiles in the swizzled layout the operand reads expect.
+  // of each tile (key lp for thread tid, lp = tid/8), and slot lc of a row
+  // receives the row's chunk lc ^ swizzle, which places the tiles in the
+  // swizzled layout the operand reads expect.
   const int lc = tid & 7;
   const int lp = tid >> 3;
   const int32_t k_col = (head * D + ((lc ^ k_swz(lp)) * 8)) * 2;
@@ -329,12 +334,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   // (the row table holds position 0's code there), and so does the padding
   // past kv_len; the test is uniform per tile, and only the step's last tiles
   // take that branch.
-  auto load_kv = [&](int32_t x, uint2 c) __attribute__((always_inline)) {
+  auto load_kv = [&](int32_t x, uint32_t c) __attribute__((always_inline)) {
     const int32_t stage = x & (NST - 1);
-    const char* k0 = row_ptr(c.x, false);
-    const char* k1 = row_ptr(c.y, false);
-    const char* v0 = row_ptr(c.x, true);
-    const char* v1 = row_ptr(c.y, true);
+    const char* k0 = row_ptr(c, false);
+    const char* v0 = row_ptr(c, true);
     const int32_t t0 = tile_at(x) * 64;
     if (TR && t0 + 64 > a.tr_start) {
       const char* tk = static_cast<const char*>(a.tk) + k_col;
@@ -342,23 +345,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
       // the padding past kv_len repeats the last own row (finite input, whose
       // weights the mask zeroes; a pool row there may be unwritten memory
       // when every key of the step is the frame's own)
-      const int32_t j0 = t0 + lp - a.tr_start, j1 = j0 + 32;
+      const int32_t j0 = t0 + lp - a.tr_start;
       const int32_t n_own = a.kv_len - a.tr_start;
       if (j0 >= 0) {
         const int32_t j = min(j0, n_own - 1);
         k0 = tk + size_t(j) * a.row_bytes;
         v0 = tv + size_t(j) * a.row_bytes;
       }
-      if (j1 >= 0) {
-        const int32_t j = min(j1, n_own - 1);
-        k1 = tk + size_t(j) * a.row_bytes;
-        v1 = tv + size_t(j) * a.row_bytes;
-      }
     }
     load_to_lds<16>(k0, &lds_k[stage][(8 * wave) * LS]);
-    load_to_lds<16>(k1, &lds_k[stage][(32 + 8 * wave) * LS]);
     load_to_lds<16>(v0, &lds_v[stage][(8 * wave) * LS]);
-    load_to_lds<16>(v1, &lds_v[stage][(32 + 8 * wave) * LS]);
   };
   // all 64 codes of tile position x into their slot (every wavefront loads
   // the whole slice, so each one waits only for its own loads)
@@ -366,8 +362,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     load_to_lds<4>(a.rowtab + tile_at(x) * 64 + lane, &lds_code[x & (NCODE - 1)][0]);
   };
   auto codes_of = [&](int32_t x) __attribute__((always_inline)) {
-    const uint32_t* c = lds_code[x & (NCODE - 1)];
-    return make_uint2(c[lp], c[lp + 32]);
+    return lds_code[x & (NCODE - 1)][lp];
   };
   // barrier without a memory fence (the fence would wait for every load
   // into LDS): each use follows an explicit wait for this wavefront's loads
@@ -385,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   // position i+kLead+1's codes have then landed (issued in step i+1-kLead or,
   // for the first steps, in the prologue); those codes are read before the
   // barrier, so their LDS latency overlaps it.
-  uint2 code_nx;  // codes of the position the next step loads
+  uint32_t code_nx;  // code of this thread's row of the position the next step loads
   auto step_loads = [&](int32_t i) __attribute__((always_inline)) {
     load_kv(i + kLead, code_nx);
     load_codes(i + 2 * kLead);
@@ -400,9 +395,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   // rows of their tiles (staged in LDS from the caller's rows) into the
   // pages the step reserved, whose codes the row table holds at the own
   // positions; the other groups only read them.  At the start of step i,
-  // while position i's stage is resident: wavefront w stores rows 16w ..
-  // 16w+15 of the tile, lane l row 16w + l/4, chunks 2(l%4) and 2(l%4)+1 of
-  // this head's K and V.  The stores count in the vector-memory counter
+  // while position i's stage is resident: wavefront w stores rows 8w ..
+  // 8w+7 of the tile, lane l row 8w + l/8, chunk l%8 of this head's K and V
+  // (the row and chunk it loaded).  The stores count in the vector-memory counter
   // beside the loads; loads still complete in order, so each step's wait for
   // its oldest loads stays sufficient.
   const bool own_store = TR && a.own_store != 0 && qt == 0;
@@ -411,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
   const int32_t own_i1 = own_store ? (a.kv_len + 63) / 64 - t_begin : own_i0;
   auto own_write = [&](int32_t i, int stage) __attribute__((always_inline)) {
     if (!TR || i < own_i0 || i >= own_i1) return;
-    const int r = 16 * wave + (lane >> 2);
+    const int r = lp;
     const int32_t key = (t_begin + i) * 64 + r;
     if (key < a.tr_start || key >= a.kv_len) return;
     const uint32_t code = lds_code[i & (NCODE - 1)][r];
@@ -421,17 +416,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_d64_kernel(const BatchArgs b
     char* kd = static_cast<char*>(const_cast<void*>(special ? a.special_pool : a.patch_pool)) +
                (code & 0x7fffffffu) + head * D * 2;
     char* vd = kd + (special ? a.vstride_special : a.vstride_patch);
-    const int c0 = 2 * (lane & 3);
-    const uint16_t* kr = &lds_k[stage][r * LS];
-    const uint16_t* vr = &lds_v[stage][r * LS];
-    const uint4 k0 = *reinterpret_cast<const uint4*>(kr + ((c0 ^ k_swz(r)) * 8));
-    const uint4 k1 = *reinterpret_cast<const uint4*>(kr + (((c0 + 1) ^ k_swz(r)) * 8));
-    const uint4 v0 = *reinterpret_cast<const uint4*>(vr + ((c0 ^ v_swz(r)) * 8));
-    const uint4 v1 = *reinterpret_cast<const uint4*>(vr + (((c0 + 1) ^ v_swz(r)) * 8));
+    const int c0 = lc;
+    const uint4 k0 = *reinterpret_cast<const uint4*>(&lds_k[stage][r * LS + ((c0 ^ k_swz(r)) * 8)]);
+    const uint4 v0 = *reinterpret_cast<const uint4*>(&lds_v[stage][r * LS + ((c0 ^ v_swz(r)) * 8)]);
     reinterpret_cast<uint4*>(kd)[c0] = k0;
-    reinterpret_cast<uint4*>(kd)[c0 + 1] = k1;
     reinterpret_cast<uint4*>(vd)[c0] = v0;
-    reinterpret_cast<uint4*>(vd)[c0 + 1] = v1;
   };
 
   // K operand: row kb*32 + l32, chunk 2ks + hh (swizzle depends on l32 only).
@@ -869,7 +858,7 @@ hipError_t launch_attn16(const BatchArgs& b, int32_t head_dim, bool fp16, bool t
   // (an append carried by the launch is stored by query group 0, own_store;
   // the launch takes no extra workgroups)
   if (b.app.wgs != 0) return hipErrorInvalidValue;
-  const dim3 grid(8 * b.items_per_xcd), block(kThreads);
+  const dim3 grid(8 * b.items_per_xcd), block(kThreads16);
   if (fp16 && transient)
     hipLaunchKernelGGL((attn_d64_kernel<_Float16, true>), grid, block, 0, stream, b);
   else if (fp16)
@@ -883,7 +872,7 @@ hipError_t launch_attn16(const BatchArgs& b, int32_t head_dim, bool fp16, bool t
 
 int32_t attn_occupancy16() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_d64_kernel<__bf16, false>, kThreads, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_d64_kernel<__bf16, false>, kThreads16, 0) !=
           hipSuccess ||
       n < 1)
     return 1;

@@ -126,9 +126,9 @@ struct BatchArgs {
   FusedAppend app;
 };
 
-// Query rows per workgroup: the 16-bit kernel (4 wavefronts x 64) and the
+// Query rows per workgroup: the 16-bit kernel (8 wavefronts x 64) and the
 // fp32 kernel (4 x 32).
-constexpr int32_t kRowsPerWG16 = kRowsPerGroup;
+constexpr int32_t kRowsPerWG16 = 2 * kRowsPerGroup;
 constexpr int32_t kRowsPerWGf32 = 128;
 static_assert(kRowsPerGroup % kRowsPerWGf32 == 0, "partial rows cover both kernels' groups");
 

@@ -219,6 +219,13 @@ def test_choose_splits():
     assert cs(1375, 99054, 16, 256, 2, 16, 0, 256) == 8
     assert cs(1375, 99054, 16, 256, 2, 16, 0, 128) == 10
     assert cs(1375, 99054, 16, 256, 2, 16, 0, -1) == 8   # non-positive: the 256-row default
+    # the 16-bit kernel with 512-row workgroups, one per CU: 5 key ranges (one
+    # dispatch round of 240 workgroups) measured best (5: 1005, 16: 989, 10:
+    # 980, 4: 903, 8: 872, 6: 666 TFLOP/s), and the model picks 5 along the
+    # stream's key lengths
+    assert cs(1375, 99054, 16, 256, 1, 16, 0, 512) == 5
+    assert cs(1375, 88054, 16, 256, 1, 16, 0, 512) == 5
+    assert cs(1375, 158568, 16, 256, 1, 16, 0, 512) == 5
 
 
 @pytest.mark.parametrize("cid", [0, 2, 4])
