@@ -54,7 +54,7 @@
 //    P rounded to the input type (round to nearest even); the V operand comes from the
 //    row-major tile through gfx950's LDS transpose reads;
 //  * at most 256 VGPRs and no scratch, one workgroup (two wavefronts per
-//    SIMD) per CU; the steady-state loop takes four steps per iteration, so
+//    SIMD) per CU; the steady-state loop takes NST steps per iteration, so
 //    LDS operand offsets are constants;
 //  * with several splits, each writes its partial (O / l rounded to the input
 //    type, and m, l in fp32) that a separate merge kernel combines (a kernel boundary orders them: no fences, which on this
@@ -775,36 +775,26 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
     step_loads(0);
     tile(nh_c, 0, true, false, 0);
     end_step(0);
-    // four steps per iteration, so that each tile's stage (i mod 4, with i = 1
-    // mod 4 at the top) is a constant and its LDS operand addresses fold into
-    // the instructions' offsets
+    // NST steps per iteration, so that each tile's stage (i mod NST, with
+    // i = 1 mod NST at the top) is a constant and its LDS operand addresses
+    // fold into the instructions' offsets
     int32_t i = 1;
     // each step reads block 0's K operands before issuing its loads, so that
     // their LDS latency overlaps the load addresses.  Tiles with own rows to
     // store go to the loop below.
     const int32_t n_fast = min(n_t, own_i0 < own_i1 ? own_i0 + 1 : n_t);
     h8 kf0[4];
-    for (; i + 4 < n_fast; i += 4) {
-      read_k(lds_k[1], 0, kf0);
-      __builtin_amdgcn_sched_barrier(0);
-      step_loads(i);
-      tile(nh_c, i, false, false, 1, kf0);
-      end_step(i);
-      read_k(lds_k[2], 0, kf0);
-      __builtin_amdgcn_sched_barrier(0);
-      step_loads(i + 1);
-      tile(nh_c, i + 1, false, false, 2, kf0);
-      end_step(i + 1);
-      read_k(lds_k[3], 0, kf0);
-      __builtin_amdgcn_sched_barrier(0);
-      step_loads(i + 2);
-      tile(nh_c, i + 2, false, false, 3, kf0);
-      end_step(i + 2);
-      read_k(lds_k[0], 0, kf0);
-      __builtin_amdgcn_sched_barrier(0);
-      step_loads(i + 3);
-      tile(nh_c, i + 3, false, false, 0, kf0);
-      end_step(i + 3);
+    for (; i + NST < n_fast; i += NST) {
+#pragma unroll
+      for (int k = 0; k < NST; ++k) {
+        constexpr int kStage0 = 1;  // i = 1 mod NST here
+        const int st = (kStage0 + k) & (NST - 1);
+        read_k(lds_k[st], 0, kf0);
+        __builtin_amdgcn_sched_barrier(0);
+        step_loads(i + k);
+        tile(nh_c, i + k, false, false, st, kf0);
+        end_step(i + k);
+      }
     }
     for (; i + 1 < n_t; ++i) {
       own_write(i, i & (NST - 1));
