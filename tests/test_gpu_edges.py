@@ -86,6 +86,57 @@ def test_tile_and_row_edges(dtype, head_dim):
         say(f"{dtype} D={D}: kv={kv} done ({n} cases), worst max-abs {worst:.3e}")
 
 
+# query counts around the 16-bit kernel's 512-row groups (the step's 32-row
+# halves dealt over ceil(Tq / 512) groups: 15/14/14 at 1375)
+TQ_GROUP_CASES = [511, 512, 513, 1024, 1025, 1375]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_query_group_edges(dtype):
+    """Query counts that fill, just exceed or split unevenly over the 16-bit
+    kernel's 512-row workgroups, on short and tile-ragged key sets, with the
+    planner's and a forced split count; every output against the oracle."""
+    D, max_q = 64, max(TQ_GROUP_CASES)
+    seed0 = 9300 + DTYPE_CODE[dtype]
+    pp = workloads.gen_normal((N_PP, 2, P, H, D), seed0 + 1, dtype, DEV)
+    sp = workloads.gen_normal((N_SP, 2, SPS, H, D), seed0 + 2, dtype, DEV)
+    q_all = workloads.gen_normal((max_q, H, D), seed0 + 3, dtype, DEV)
+    rng = np.random.default_rng(seed0)
+    pid = rng.permutation(N_PP).astype(np.int32)
+    sid = rng.permutation(N_SP).astype(np.int32)
+    pid_d = torch.from_numpy(pid).to(DEV)
+    sid_d = torch.from_numpy(sid).to(DEV)
+    pp_h, sp_h = pp.double().cpu().numpy(), sp.double().cpu().numpy()
+    q_h = q_all.double().cpu().numpy()
+    stream = torch.cuda.current_stream().cuda_stream
+    worst = 0.0
+    for n_pp, n_st in [(0, 65), (2, 27), (10, 191)]:
+        k_rows = [pp_h[p, 0] for p in pid[:n_pp]] + [sp_h[s, 0] for s in sid]
+        v_rows = [pp_h[p, 1] for p in pid[:n_pp]] + [sp_h[s, 1] for s in sid]
+        kv = n_pp * P + n_st
+        K = np.concatenate(k_rows)[:kv]
+        V = np.concatenate(v_rows)[:kv]
+        for tq in TQ_GROUP_CASES:
+            ref = dense_attention(q_h[:tq], K, V)
+            q = q_all[:tq].contiguous()
+            for splits in [0, 3]:
+                cfg = lbm.make_config(num_blocks=1, num_heads=H, head_dim=D, patches_per_frame=P,
+                                      special_per_frame=6, special_page_size=SPS, scale_frames=2,
+                                      sliding_window=8, max_patch_pages=N_PP, max_special_pages=N_SP,
+                                      max_frames_per_step=1, max_q_tokens=max_q,
+                                      dtype=DTYPE_CODE[dtype], num_splits=splits)
+                ws = torch.empty(lbm.lbm_query_sizes(cfg)[2], dtype=torch.uint8, device=DEV)
+                out = torch.full_like(q, float("nan"))
+                lbm.lbm_paged_attention(cfg, q.data_ptr(), out.data_ptr(), tq, pp.data_ptr(),
+                                        sp.data_ptr(), pid_d.data_ptr(), n_pp, sid_d.data_ptr(),
+                                        n_st, ws.data_ptr(), stream)
+                torch.cuda.synchronize()
+                st = compare(out.double().cpu().numpy(), ref, dtype,
+                             f"{dtype} kv={kv} tq={tq} splits={splits}")
+                worst = max(worst, st["max_abs"])
+    say(f"{dtype} query-group edges: worst max-abs {worst:.3e}")
+
+
 def test_empty_visible_set_is_rejected():
     cfg = _config("bf16", 64, 0)
     ws = torch.empty(lbm.lbm_query_sizes(cfg)[2], dtype=torch.uint8, device=DEV)
