@@ -40,11 +40,20 @@ lbm_status lbmcore_stats(const lbmcore* core, lbm_stats* out);
 
 /* The planner's key-range split choice for a run of num_q_tokens queries
  * over kv_len keys by a kernel whose workgroups hold rows_per_wg query rows
- * (0: the 16-bit kernel's 256; the fp32 kernel's are 128): returns the split
- * count (>= 1), or a negative status. */
+ * (0: 256; the 16-bit kernel's hold 512, the fp32 kernel's 128), with the
+ * fewest query groups that hold the rows: returns the split count (>= 1), or
+ * a negative status. */
 int32_t lbmcore_choose_splits(int32_t num_q_tokens, int32_t kv_len, int32_t num_heads,
                               int32_t num_cu, int32_t wg_per_cu, int32_t split_cap,
                               int32_t forced, int32_t rows_per_wg);
+
+/* The same choice with the number of query groups chosen as well (the fewest
+ * that hold the rows, or one more; the 16-bit kernel's launches): returns the
+ * split count and writes the groups to *groups (non-null), or returns a
+ * negative status. */
+int32_t lbmcore_choose_launch(int32_t num_q_tokens, int32_t kv_len, int32_t num_heads,
+                              int32_t num_cu, int32_t wg_per_cu, int32_t split_cap,
+                              int32_t forced, int32_t rows_per_wg, int32_t* groups);
 
 const char* lbmcore_last_error(void);
 

@@ -457,6 +457,15 @@ class CoreBookkeeping:
         return core_lib().lbmcore_choose_splits(num_q_tokens, kv_len, num_heads, num_cu,
                                                 wg_per_cu, split_cap, forced, rows_per_wg)
 
+    @staticmethod
+    def choose_launch(num_q_tokens, kv_len, num_heads, num_cu, wg_per_cu, split_cap, forced=0,
+                      rows_per_wg=0):
+        """(splits, query groups) as the 16-bit kernel's launches choose them."""
+        g = c_int32(0)
+        ns = core_lib().lbmcore_choose_launch(num_q_tokens, kv_len, num_heads, num_cu, wg_per_cu,
+                                              split_cap, forced, rows_per_wg, byref(g))
+        return ns, g.value
+
 
 class StepGraph:
     """A frame step replayed as one HIP graph over fixed buffers: fill the

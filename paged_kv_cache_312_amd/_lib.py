@@ -97,6 +97,7 @@ CORE_FUNCS = {
     "lbmcore_dump": (c_int32, [c_void_p, POINTER(c_int32), c_int64, POINTER(c_int64)]),
     "lbmcore_stats": (c_int32, [c_void_p, POINTER(LbmStats)]),
     "lbmcore_choose_splits": (c_int32, [c_int32] * 8),
+    "lbmcore_choose_launch": (c_int32, [c_int32] * 8 + [POINTER(c_int32)]),
     "lbmcore_last_error": (c_char_p, []),
 }
 

@@ -292,7 +292,8 @@ void Bookkeeping::plan_record(std::vector<int32_t>* out) const {
 // ---------------------------------------------------------------------------
 
 int32_t choose_splits(int32_t num_q_tokens, int32_t kv_len, int32_t num_heads, int32_t num_cu,
-                      int32_t wg_per_cu, int32_t split_cap, int32_t forced, int32_t rows_per_wg) {
+                      int32_t wg_per_cu, int32_t split_cap, int32_t forced, int32_t rows_per_wg,
+                      int32_t* groups) {
   if (num_q_tokens < 1 || kv_len < 1 || num_heads < 1 || num_cu < 1 || wg_per_cu < 1 ||
       split_cap < 1 || rows_per_wg < 1)
     return LBM_ERR_INVALID_ARG;
@@ -302,36 +303,49 @@ int32_t choose_splits(int32_t num_q_tokens, int32_t kv_len, int32_t num_heads, i
     const int32_t tps = ceil_div(n_tiles, ns);
     return ceil_div(n_tiles, tps);  // no empty split
   };
+  const int32_t q_min = ceil_div(num_q_tokens, rows_per_wg);
+  const int32_t n_half = ceil_div(num_q_tokens, 32);
+  const int32_t q_max = groups ? std::min(q_min + 1, std::max(n_half, q_min)) : q_min;
+  if (groups) *groups = q_min;
   if (forced > 0) return normalise(std::min(forced, cap));
-  // Cost model, in tile-times of one workgroup alone on a CU, fitted to the
-  // 16-bit kernel (256 query rows per workgroup) on MI355X and applied to
+  // Cost model, in tile-times of one full workgroup alone on a CU, fitted to
+  // the 16-bit kernel (256 query rows per workgroup) on MI355X and applied to
   // either kernel's workgroups (the fp32 kernel's hold 128 rows): k workgroups
   // sharing a CU each take 1 + 0.85 (k - 1) per tile (a second workgroup
   // mostly hides latency; the CU's throughput grows little); every workgroup
   // pays a start/finish cost of about 2 tiles; splitting adds a merge pass (a
   // launch, ~13 tiles, plus ~4 tiles per split of partials).  Equal
   // workgroups are dispatched in rounds of num_cu * wg_per_cu; the last,
-  // partial round spreads its workgroups over the CUs.
+  // partial round spreads its workgroups over the CUs.  Choosing groups, a
+  // group of g halves takes ceil(g / 4) / ceil(g_full / 4) of a full group's
+  // tile time (its busiest SIMD's share; g_full = rows_per_wg / 32).
   constexpr double kShare = 0.85, kFixed = 2.0, kMergeLaunch = 13.0, kMergePerSplit = 4.0;
-  const int64_t units = int64_t(ceil_div(num_q_tokens, rows_per_wg)) * num_heads;
   const int64_t slots = int64_t(num_cu) * wg_per_cu;
+  const int32_t simd_full = std::max(1, ceil_div(rows_per_wg / 32, 4));
   auto per_tile = [&](int64_t k) { return 1.0 + kShare * double(k - 1); };
-  int32_t best = 1;
+  int32_t best = 1, best_q = q_min;
   double best_cost = std::numeric_limits<double>::infinity();
-  for (int32_t ns = 1; ns <= cap; ++ns) {
-    const int32_t n = normalise(ns);
-    if (n != ns) continue;
-    const double len = double(ceil_div(n_tiles, n)) + kFixed;
-    const int64_t wgs = units * n;
-    const int64_t full = wgs / slots, rest = wgs % slots;
-    double cost = double(full) * len * per_tile(wg_per_cu);
-    if (rest > 0) cost += len * per_tile((rest + num_cu - 1) / num_cu);
-    if (n > 1) cost += kMergeLaunch + kMergePerSplit * n;
-    if (cost < best_cost - 1e-9) {
-      best_cost = cost;
-      best = n;
+  for (int32_t nq = q_min; nq <= q_max; ++nq) {
+    const double load =
+        groups ? double(ceil_div(ceil_div(n_half, nq), 4)) / double(simd_full) : 1.0;
+    const int64_t units = int64_t(nq) * num_heads;
+    for (int32_t ns = 1; ns <= cap; ++ns) {
+      const int32_t n = normalise(ns);
+      if (n != ns) continue;
+      const double len = (double(ceil_div(n_tiles, n)) + kFixed) * std::min(1.0, load);
+      const int64_t wgs = units * n;
+      const int64_t full = wgs / slots, rest = wgs % slots;
+      double cost = double(full) * len * per_tile(wg_per_cu);
+      if (rest > 0) cost += len * per_tile((rest + num_cu - 1) / num_cu);
+      if (n > 1) cost += kMergeLaunch + kMergePerSplit * n;
+      if (cost < best_cost - 1e-9) {
+        best_cost = cost;
+        best = n;
+        best_q = nq;
+      }
     }
   }
+  if (groups) *groups = best_q;
   return best;
 }
 

@@ -117,10 +117,14 @@ class Bookkeeping {
 // Split count for one run: how many key ranges each (query group, head) is
 // cut into so that the launch fills the chip (>= 1).  `forced` > 0 asks for
 // that many (capped); `split_cap` bounds the choice; `rows_per_wg` is the
-// query rows of one workgroup of the kernel that will run.
+// query rows of one workgroup of the kernel that will run.  With `groups`,
+// the query groups are chosen too (the fewest that hold the rows, or one
+// more), written there: a workgroup's step time is taken to follow its
+// busiest SIMD, which holds ceil(halves / 4) of the group's 32-row halves
+// (four SIMDs per CU); without it the groups are the fewest.
 int32_t choose_splits(int32_t num_q_tokens, int32_t kv_len, int32_t num_heads, int32_t num_cu,
                       int32_t wg_per_cu, int32_t split_cap, int32_t forced,
-                      int32_t rows_per_wg = kRowsPerGroup);
+                      int32_t rows_per_wg = kRowsPerGroup, int32_t* groups = nullptr);
 
 // Workspace layout (byte offsets from the workspace base).
 // Per-step values of a frame step that graph-replayed launches read from

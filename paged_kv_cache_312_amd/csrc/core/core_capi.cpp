@@ -119,6 +119,14 @@ int32_t lbmcore_choose_splits(int32_t num_q_tokens, int32_t kv_len, int32_t num_
                             rows_per_wg > 0 ? rows_per_wg : lbm::kRowsPerGroup);
 }
 
+int32_t lbmcore_choose_launch(int32_t num_q_tokens, int32_t kv_len, int32_t num_heads,
+                              int32_t num_cu, int32_t wg_per_cu, int32_t split_cap,
+                              int32_t forced, int32_t rows_per_wg, int32_t* groups) {
+  if (!groups) return LBM_ERR_INVALID_ARG;
+  return lbm::choose_splits(num_q_tokens, kv_len, num_heads, num_cu, wg_per_cu, split_cap, forced,
+                            rows_per_wg > 0 ? rows_per_wg : lbm::kRowsPerGroup, groups);
+}
+
 const char* lbmcore_last_error(void) { return lbm::last_error(); }
 
 }  // extern "C"

@@ -32,11 +32,15 @@ int32_t attn_occupancy(int32_t dtype, int32_t head_dim) {
 
 int32_t partial_rows(int32_t Tq) { return (Tq + kRowsPerGroup - 1) / kRowsPerGroup * kRowsPerGroup; }
 
-void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits, int32_t rows_per_wg) {
+void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits, int32_t rows_per_wg,
+                      int32_t groups) {
   a->n_tiles = (a->kv_len + kKeysPerTile - 1) / kKeysPerTile;
   a->tiles_per_split = (a->n_tiles + num_splits - 1) / num_splits;
   a->num_splits = (a->n_tiles + a->tiles_per_split - 1) / a->tiles_per_split;
-  a->n_qt = (a->Tq + rows_per_wg - 1) / rows_per_wg;
+  // query groups: the planner's (16-bit kernel), never fewer than hold the
+  // rows nor more than the rows' 32-row halves
+  const int32_t q_min = (a->Tq + rows_per_wg - 1) / rows_per_wg;
+  a->n_qt = std::min(std::max(groups, q_min), std::max(q_min, (a->Tq + 31) / 32));
   a->rows_pad = partial_rows(a->Tq);
   a->total_items = a->n_qt * a->H * a->num_splits;
   a->items_per_xcd = (a->total_items + 7) / 8;
@@ -91,6 +95,7 @@ struct lbm_cache {
   uint64_t plan_epoch = 0;
   int32_t plan_q = 0;
   int32_t plan_splits = 0;
+  int32_t plan_groups = 0;    // query groups of the plan's launches (0: the fewest)
   int32_t plan_own = 0;       // own rows of a skip-append step planned (0: a normal plan)
   bool plan_fused = false;    // the own rows are the open step's frames (lbm_append_run)
   PlanInfo plan;
@@ -109,6 +114,7 @@ struct lbm_cache {
 struct lbm_graph {
   lbm_cache* c = nullptr;
   int32_t nf = 0, nq = 0, ns = 0;
+  int32_t groups = 0;  // query groups of the captured launches (0: the fewest)
   size_t bytes = 0;                 // staging = workspace [desc_off, special ids end)
   hipStream_t cap_stream = nullptr;
   hipGraph_t graph[2] = {nullptr, nullptr};
@@ -199,12 +205,13 @@ AttnArgs base_args(const lbm_config& c, const void* q, void* out, int32_t nq, co
 // c's head_dim and dtype, all with or all without own rows), then the merge
 // of every stream whose key range is split.
 lbm_status launch_attention_batch(const lbm_config& c, AttnArgs* as, int32_t n, int32_t splits,
-                                  hipStream_t st, const FusedAppend* app = nullptr) {
+                                  hipStream_t st, const FusedAppend* app = nullptr,
+                                  int32_t groups = 0) {
   BatchArgs b;
   std::memset(&b, 0, sizeof(b));
   b.n = n;
   for (int32_t i = 0; i < n; ++i) {
-    finish_attn_args(&as[i], c.head_dim, splits, kernel_rows_per_wg(c.dtype));
+    finish_attn_args(&as[i], c.head_dim, splits, kernel_rows_per_wg(c.dtype), groups);
     b.s[i] = as[i];
     b.item_start[i + 1] = b.item_start[i] + as[i].total_items;
   }
@@ -228,9 +235,12 @@ lbm_status launch_attention_batch(const lbm_config& c, AttnArgs* as, int32_t n, 
 }
 
 lbm_status launch_attention(const lbm_config& c, AttnArgs* a, int32_t splits, hipStream_t st,
-                            const FusedAppend* app = nullptr) {
-  return launch_attention_batch(c, a, 1, splits, st, app);
+                            const FusedAppend* app = nullptr, int32_t groups = 0) {
+  return launch_attention_batch(c, a, 1, splits, st, app, groups);
 }
+
+// the planner's query groups are chosen for the 16-bit kernel only
+int32_t* groups_out(int32_t dtype, int32_t* g) { return dtype == LBM_F32 ? nullptr : g; }
 
 }  // namespace
 
@@ -342,10 +352,12 @@ lbm_status paged_attention_impl(const lbm_config* cfg, const void* q, void* out,
   int dev = 0, ncu = 256;
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  int32_t groups = 0;
   const int32_t ns = choose_splits(num_q_tokens, a.kv_len, cfg->num_heads, ncu,
                                    attn_occupancy(cfg->dtype, cfg->head_dim), cap,
-                                   cfg->num_splits, kernel_rows_per_wg(cfg->dtype));
-  return launch_attention(*cfg, &a, ns < 1 ? 1 : ns, stream);
+                                   cfg->num_splits, kernel_rows_per_wg(cfg->dtype),
+                                   groups_out(cfg->dtype, &groups));
+  return launch_attention(*cfg, &a, ns < 1 ? 1 : ns, stream, nullptr, groups);
 }
 
 }  // namespace
@@ -602,13 +614,15 @@ lbm_status plan_impl(lbm_cache* c, int32_t num_q_tokens, int32_t own, void* hip_
   if (rs != LBM_OK) return rs;
 
   const int32_t cap = split_capacity(c->ws, num_q_tokens);
+  int32_t groups = 0;
   int32_t ns = choose_splits(num_q_tokens, p.kv_len + own, c->cfg.num_heads, c->num_cu,
                              c->wg_per_cu, cap, c->cfg.num_splits,
-                             kernel_rows_per_wg(c->cfg.dtype));
+                             kernel_rows_per_wg(c->cfg.dtype), groups_out(c->cfg.dtype, &groups));
   if (ns < 1) ns = 1;
   c->plan = p;
   c->plan_q = num_q_tokens;
   c->plan_splits = ns;
+  c->plan_groups = groups;
   c->plan_own = own;
   c->plan_fused = fused_nf > 0;
   c->plan_epoch = c->bk.epoch();
@@ -669,7 +683,8 @@ lbm_status lbm_run(lbm_cache* c, int32_t block_idx, const void* q, void* out,
                          c->workspace, c->ws);
   a.kv_len = c->plan.kv_len;
   a.tr_start = a.kv_len;
-  return launch_attention(c->cfg, &a, c->plan_splits, static_cast<hipStream_t>(hip_stream));
+  return launch_attention(c->cfg, &a, c->plan_splits, static_cast<hipStream_t>(hip_stream),
+                          nullptr, c->plan_groups);
 }
 
 lbm_status lbm_run_transient(lbm_cache* c, int32_t block_idx, const void* q, const void* k,
@@ -696,7 +711,8 @@ lbm_status lbm_run_transient(lbm_cache* c, int32_t block_idx, const void* q, con
   a.kv_len = c->plan.kv_len + c->plan_own;
   a.tk = k;
   a.tv = v;
-  return launch_attention(c->cfg, &a, c->plan_splits, static_cast<hipStream_t>(hip_stream));
+  return launch_attention(c->cfg, &a, c->plan_splits, static_cast<hipStream_t>(hip_stream),
+                          nullptr, c->plan_groups);
 }
 
 lbm_status lbm_append_run(lbm_cache* c, int32_t block_idx, const void* q, const void* k,
@@ -796,7 +812,7 @@ lbm_status lbm_append_run(lbm_cache* c, int32_t block_idx, const void* q, const 
     // stages (their destinations are the row table's own codes)
     a.own_store = 1;
   }
-  st = launch_attention(c->cfg, &a, c->plan_splits, s, &f);
+  st = launch_attention(c->cfg, &a, c->plan_splits, s, &f, c->plan_groups);
   if (st != LBM_OK) return st;
   c->appended[size_t(block_idx)] = 1;
   return LBM_OK;
@@ -979,7 +995,7 @@ lbm_status graph_capture(lbm_graph* g, int i, const void* const* k, const void* 
     a.kv_len = g->ns * kKeysPerTile;
     a.tr_start = a.kv_len;
     a.desc = desc;
-    st = launch_attention(cfg, &a, g->ns, g->cap_stream);
+    st = launch_attention(cfg, &a, g->ns, g->cap_stream, nullptr, g->groups);
   }
   hipGraph_t graph = nullptr;
   e = hipStreamEndCapture(g->cap_stream, &graph);
@@ -1027,7 +1043,7 @@ lbm_status lbm_graph_create(lbm_cache* c, int32_t num_frames, const void* const*
                              c->cfg.patches_per_frame + c->bk.plan_info().special_tokens + nq;
   g->ns = choose_splits(nq, int32_t(std::min<int64_t>(kv_est, kMaxKvLen - 1)), c->cfg.num_heads,
                         c->num_cu, c->wg_per_cu, split_capacity(c->ws, nq), c->cfg.num_splits,
-                        kernel_rows_per_wg(c->cfg.dtype));
+                        kernel_rows_per_wg(c->cfg.dtype), groups_out(c->cfg.dtype, &g->groups));
   if (g->ns < 1) g->ns = 1;
   g->bytes = c->ws.special_ids_off + sizeof(int32_t) * size_t(std::max(1, c->cfg.max_special_pages)) -
              c->ws.desc_off;

@@ -56,8 +56,8 @@
 //  * at most 256 VGPRs and no scratch, one workgroup (two wavefronts per
 //    SIMD) per CU; the steady-state loop takes NST steps per iteration, so
 //    LDS operand offsets are constants;
-//  * with several splits, each writes its partial (O / l rounded to the input
-//    type, and m, l in fp32) that a separate merge kernel combines (a kernel boundary orders them: no fences, which on this
+//  * with several splits, each writes its partial (O, m, l in fp32) that a
+//    separate merge kernel combines (a kernel boundary orders them: no fences, which on this
 //    chip would write back and invalidate the XCD's L2 that the workgroups
 //    share);
 //  * one launch may cover several independent streams (a table of per-stream
@@ -244,15 +244,35 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
   // Rows: the step's ceil(Tq / 32) halves of 32 rows are dealt to the n_qt
   // query groups as evenly as whole halves allow (base or base + 1 each, the
   // larger groups first), so that the groups sharing a key range do equal
-  // work and stay in step on its tiles; wavefront w takes halves 2w and
-  // 2w + 1 of its group while the group has them (nh of them: 2, 1 or 0).
-  // This lane's row in half h is qrow0 + 32h.
+  // work and stay in step on its tiles.  Within a group, wavefronts w and
+  // w + 4 share SIMD w mod 4 and the workgroup's step time follows its
+  // busiest SIMD, so the g halves go to the SIMDs first: c_s to SIMD s, at
+  // most L = ceil(g / 4) each, the shortfall 4L - g taken where it leaves
+  // the fewest odd counts (a wavefront with one half reads as many operands
+  // as one with two).  SIMD s takes halves [S_s, S_s + c_s) of the group
+  // (S_s = c_0 + .. + c_(s-1)): wavefront s the first two, wavefront s + 4
+  // the rest (nh of them: 2, 1 or 0); this lane's row in half h is
+  // qrow0 + 32h.
   const int32_t n_half = (a.Tq + 31) / 32;
   const int32_t base = n_half / a.n_qt, rem = n_half - base * a.n_qt;
   const int32_t g_halves = base + (qt < rem ? 1 : 0);
-  const int32_t nh = __builtin_amdgcn_readfirstlane(min(max(g_halves - 2 * wave, 0), 2));
-  const int32_t w_row0 = 32 * (base * qt + min(qt, rem) + 2 * wave);
-  const int32_t qrow0 = w_row0 + l32;
+  int32_t nh, qrow0;
+  {
+    const int32_t L = (g_halves + 3) / 4, e = 4 * L - g_halves;
+    int32_t c[4] = {L, L, L, L};
+    if (L % 2 == 0) {
+      if (e >= 2) c[3] -= 2;
+      if (e % 2) c[e >= 2 ? 2 : 3] -= 1;
+    } else {
+      for (int k = 0; k < 3; ++k)
+        if (k < e) c[3 - k] -= 1;
+    }
+    const int sm = wave & 3, hi = wave >> 2;
+    const int32_t S = (sm > 0 ? c[0] : 0) + (sm > 1 ? c[1] : 0) + (sm > 2 ? c[2] : 0);
+    const int32_t cs = sm == 0 ? c[0] : sm == 1 ? c[1] : sm == 2 ? c[2] : c[3];
+    nh = __builtin_amdgcn_readfirstlane(min(max(cs - 2 * hi, 0), 2));
+    qrow0 = 32 * (base * qt + min(qt, rem) + S + 2 * hi) + l32;
+  }
   if (t_end <= t_begin) {
     // a split left without keys (graph-replayed steps keep the capture's split
     // count): an empty partial, weight 0 in the merge
@@ -261,12 +281,12 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
       const int32_t qrow = qrow0 + 32 * h;
       if (h < nh && qrow < a.Tq) {
         const size_t rh = (size_t(split) * a.rows_pad + qrow) * a.H + head;
-        T* po = reinterpret_cast<T*>(a.part_o) + rh * D;
+        float* po = a.part_o + rh * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint2*>(po + db * 32 + 8 * i + 4 * hh) = make_uint2(0u, 0u);
+            *reinterpret_cast<float4*>(po + db * 32 + 8 * i + 4 * hh) = make_float4(0.f, 0.f, 0.f, 0.f);
         if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + rh * 2) = make_float2(-INFINITY, 0.f);
       }
     }
@@ -818,25 +838,35 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
     const int32_t qrow = qrow0 + 32 * h;
     if (h >= nh || qrow >= a.Tq) continue;
     const float l_tot = l_run[h] + __shfl_xor(l_run[h], 32);
-    // the output (one split), or the split's normalised partial O / l in T
-    // beside its (m, l) in fp32 (several splits; the merge weighs each by l)
-    const float inv = 1.f / l_tot;
-    const size_t rh = (size_t(split) * a.rows_pad + qrow) * a.H + head;
-    T* op = a.num_splits == 1
-                ? reinterpret_cast<T*>(a.out) + size_t(qrow) * HD + head * D
-                : reinterpret_cast<T*>(a.part_o) + rh * D;
+    if (a.num_splits == 1) {
+      // the output, rounded once to T
+      const float inv = 1.f / l_tot;
+      T* op = reinterpret_cast<T*>(a.out) + size_t(qrow) * HD + head * D;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+      for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        typedef T h4 __attribute__((ext_vector_type(4)));
-        h4 w;
+        for (int i = 0; i < 4; ++i) {
+          typedef T h4 __attribute__((ext_vector_type(4)));
+          h4 w;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = static_cast<T>(o[h][db][4 * i + j] * inv);
-        *reinterpret_cast<h4*>(op + db * 32 + 8 * i + 4 * hh) = w;
-      }
-    if (a.num_splits > 1 && hh == 0)
-      *reinterpret_cast<float2*>(a.part_ml + rh * 2) = make_float2(m_run[h], l_tot);
+          for (int j = 0; j < 4; ++j) w[j] = static_cast<T>(o[h][db][4 * i + j] * inv);
+          *reinterpret_cast<h4*>(op + db * 32 + 8 * i + 4 * hh) = w;
+        }
+    } else {
+      // the split's partial: O unnormalised in fp32 beside (m, l) (an output
+      // near V's own values, rounded to T here and again after the merge,
+      // would carry two roundings of up to half an ulp of T each)
+      const size_t rh = (size_t(split) * a.rows_pad + qrow) * a.H + head;
+      float* po = a.part_o + rh * D;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<float4*>(po + db * 32 + 8 * i + 4 * hh) =
+              make_float4(o[h][db][4 * i], o[h][db][4 * i + 1], o[h][db][4 * i + 2],
+                          o[h][db][4 * i + 3]);
+      if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + rh * 2) = make_float2(m_run[h], l_tot);
+    }
   }
 }
 

@@ -62,8 +62,7 @@ struct AttnArgs {
   const void* patch_pool;     // [pages][2][P][H][D]
   const void* special_pool;   // [pages][2][SPS][H][D]
   const uint32_t* rowtab;     // [n_tiles * 64] row codes (see RowtabArgs)
-  float* part_o;              // [splits][rows_pad][H][D] partial outputs: unnormalised fp32 (fp32
-                              // kernel) or O / l in the 16-bit input type (16-bit kernels)
+  float* part_o;              // [splits][rows_pad][H][D] partial outputs, unnormalised, fp32
   float* part_ml;             // [splits][rows_pad][H][2] (running max in base-2 units, partial sum)
   int32_t Tq, H;
   int32_t vstride_patch;      // bytes from a K row to its V row: P * H * D * elt
@@ -137,8 +136,10 @@ static_assert(kRowsPerGroup % kRowsPerWGf32 == 0, "partial rows cover both kerne
 int32_t partial_rows(int32_t Tq);
 
 // Fill the split/grid fields of `a` for a launch (Tq, kv_len, splits known)
-// by a kernel with `rows_per_wg` query rows per workgroup.
-void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits, int32_t rows_per_wg);
+// by a kernel with `rows_per_wg` query rows per workgroup, in `groups` query
+// groups (0: the fewest that hold the rows).
+void finish_attn_args(AttnArgs* a, int32_t head_dim, int32_t num_splits, int32_t rows_per_wg,
+                      int32_t groups = 0);
 
 // 16-bit inputs: bf16, or fp16 when `fp16`; `transient`: a skip-append step
 // (tr_start < kv_len)

@@ -5,24 +5,21 @@
 // result is out = sum_s w_s O_s / sum_s w_s l_s with w_s = 2^(m_s - M),
 // M = max_s m_s -- the usual combination of online-softmax partials (each
 // O_s and l_s is relative to its own m_s; maxima are kept in base-2 exponent
-// units, i.e. raw scores times log2(e)/sqrt(D)).  The fp32 kernel stores O_s
-// unnormalised in fp32; the 16-bit kernels store O_s / l_s rounded to their
-// input type (half the bytes; its range is that of V), which enters here
-// weighted by w_s l_s.
-// Memory-bound: one thread per 16 bytes of each partial row (8 columns of a
-// 16-bit partial, 4 of an fp32 one) of one (row, head), which issues the
-// loads of up to eight splits' partials together and then combines them (a
-// loop that loaded one split per iteration would wait out one memory latency
-// per split), and writes its columns with one 16-byte store.
+// units, i.e. raw scores times log2(e)/sqrt(D)).  Every kernel stores O_s
+// unnormalised in fp32 (a partial rounded to a 16-bit type, then the output
+// again, would round a value near V's own twice).
+// Memory-bound: one thread per 16 bytes (4 columns) of each partial row of one
+// (row, head), which issues the loads of up to eight splits' partials together
+// and then combines them (a loop that loaded one split per iteration would wait
+// out one memory latency per split), and writes its columns with one store.
 #include "attn_common.h"
 
 namespace lbm {
 namespace {
 
-// PartT: float (unnormalised O_s) or the 16-bit input type (O_s / l_s)
-template <typename OutT, typename PartT, int D>
+template <typename OutT, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
-  constexpr bool kNorm = sizeof(PartT) == 2;
+  typedef float PartT;
   constexpr int CW = 16 / sizeof(PartT);  // columns per thread
   constexpr int CPR = D / CW;             // threads per (row, head)
   constexpr int kBatch = 8;               // splits loaded together
@@ -65,9 +62,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
     for (int c = 0; c < CW; ++c) acc[c] *= r;
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const float wl = fast_exp2(ml[j].x - Mb) * ml[j].y;
-      const float w = kNorm ? wl : fast_exp2(ml[j].x - Mb);
-      den += wl;
+      const float w = fast_exp2(ml[j].x - Mb);
+      den += w * ml[j].y;
 #pragma unroll
       for (int c = 0; c < CW; ++c) acc[c] += w * float(o[j][c]);
     }
@@ -83,17 +79,16 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
 }  // namespace
 
 hipError_t launch_merge(const AttnArgs& a, int32_t head_dim, int32_t dtype, hipStream_t stream) {
-  const int32_t cw = dtype == LBM_F32 ? 4 : 8;  // columns per thread (16 bytes of partial)
-  const int64_t total = int64_t(a.Tq) * a.H * (head_dim / cw);
+  const int64_t total = int64_t(a.Tq) * a.H * (head_dim / 4);  // 4 columns per thread
   const dim3 grid(uint32_t((total + 255) / 256)), block(256);
   if (dtype == LBM_BF16 && head_dim == 64)
-    hipLaunchKernelGGL((merge_kernel<__bf16, __bf16, 64>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((merge_kernel<__bf16, 64>), grid, block, 0, stream, a);
   else if (dtype == LBM_F16 && head_dim == 64)
-    hipLaunchKernelGGL((merge_kernel<_Float16, _Float16, 64>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((merge_kernel<_Float16, 64>), grid, block, 0, stream, a);
   else if (dtype == LBM_F32 && head_dim == 64)
-    hipLaunchKernelGGL((merge_kernel<float, float, 64>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((merge_kernel<float, 64>), grid, block, 0, stream, a);
   else if (dtype == LBM_F32 && head_dim == 32)
-    hipLaunchKernelGGL((merge_kernel<float, float, 32>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((merge_kernel<float, 32>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

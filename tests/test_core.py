@@ -226,6 +226,16 @@ def test_choose_splits():
     assert cs(1375, 99054, 16, 256, 1, 16, 0, 512) == 5
     assert cs(1375, 88054, 16, 256, 1, 16, 0, 512) == 5
     assert cs(1375, 158568, 16, 256, 1, 16, 0, 512) == 5
+    # choosing the query groups too (the 16-bit kernel's launches): 4 groups
+    # of 11/11/11/10 halves (busiest SIMD 3 halves instead of 4) x 4 key
+    # ranges = 256 workgroups, every CU busy
+    cl = CoreBookkeeping.choose_launch
+    for kv in (88054, 99054, 158568):
+        assert cl(1375, kv, 16, 256, 1, 16, 0, 512) == (4, 4)
+    assert cl(1375, 99054, 16, 256, 1, 16, 6, 512) == (6, 3)   # forced splits: the fewest groups
+    assert cl(1, 1584, 2, 256, 1, 16, 0, 512)[1] == 1           # one row: one group
+    ns, g = cl(300, 1584, 2, 256, 1, 16, 0, 512)
+    assert 1 <= g <= 2 and ns >= 1
 
 
 @pytest.mark.parametrize("cid", [0, 2, 4])
