@@ -353,13 +353,15 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
   // a fused append): keys in [tr_start, kv_len) come from the frame's own rows
   // (the row table holds position 0's code there), and so does the padding
   // past kv_len; the test is uniform per tile, and only the step's last tiles
-  // take that branch.
-  auto load_kv = [&](int32_t x, uint32_t c) __attribute__((always_inline)) {
+  // take that branch.  tr_c: whether the test is made (steps that load no
+  // own row leave it out).
+  const std::integral_constant<bool, TR> tr{};
+  auto load_kv = [&](auto tr_c, int32_t x, uint32_t c) __attribute__((always_inline)) {
     const int32_t stage = x & (NST - 1);
     const char* k0 = row_ptr(c, false);
     const char* v0 = row_ptr(c, true);
     const int32_t t0 = tile_at(x) * 64;
-    if (TR && t0 + 64 > a.tr_start) {
+    if (decltype(tr_c)::value && t0 + 64 > a.tr_start) {
       const char* tk = static_cast<const char*>(a.tk) + k_col;
       const char* tv = static_cast<const char*>(a.tv) + v_col;
       // the padding past kv_len repeats the last own row (finite input, whose
@@ -401,8 +403,8 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
   // for the first steps, in the prologue); those codes are read before the
   // barrier, so their LDS latency overlaps it.
   uint32_t code_nx;  // code of this thread's row of the position the next step loads
-  auto step_loads = [&](int32_t i) __attribute__((always_inline)) {
-    load_kv(i + kLead, code_nx);
+  auto step_loads = [&](int32_t i, auto tr_c) __attribute__((always_inline)) {
+    load_kv(tr_c, i + kLead, code_nx);
     load_codes(i + 2 * kLead);
   };
   auto end_step = [&](int32_t i) __attribute__((always_inline)) {
@@ -414,12 +416,13 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
   // lbm_append_run: the workgroups of query group 0 store the frame's own
   // rows of their tiles (staged in LDS from the caller's rows) into the
   // pages the step reserved, whose codes the row table holds at the own
-  // positions; the other groups only read them.  At the start of step i,
-  // while position i's stage is resident: wavefront w stores rows 8w ..
-  // 8w+7 of the tile, lane l row 8w + l/8, chunk l%8 of this head's K and V
-  // (the row and chunk it loaded).  The stores count in the vector-memory counter
-  // beside the loads; loads still complete in order, so each step's wait for
-  // its oldest loads stays sufficient.
+  // positions; the other groups only read them.  In step i (at its start,
+  // or at its end in the unrolled loop), while position i's stage is
+  // resident: wavefront w stores rows 8w .. 8w+7 of the tile, lane l row
+  // 8w + l/8, chunk l%8 of this head's K and V (the row and chunk it
+  // loaded).  The stores count in the vector-memory counter beside the
+  // loads; loads still complete in order, so each step's wait for its oldest
+  // loads stays sufficient.
   const bool own_store = TR && a.own_store != 0 && qt == 0;
   // the steps whose tiles hold own rows: [own_i0, own_i1), empty without
   const int32_t own_i0 = a.tr_start / 64 - t_begin;
@@ -767,17 +770,25 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
   LBM_WAIT_VMCNT(0);
   asm volatile("" ::: "memory");  // the code reads below stay after the wait
 #pragma unroll
-  for (int x = 0; x < kLead; ++x) load_kv(x, codes_of(x));
+  for (int x = 0; x < kLead; ++x) load_kv(tr, x, codes_of(x));
   LBM_WAIT_VMCNT_LDS0(kLoadsKV * (kLead - 1));
   barrier();
   code_nx = codes_of(kLead);
 
+  // Steps before n_plain - 1 neither load (kLead ahead) nor store own rows:
+  // they take the loads without the test for them.
+  const int32_t n_plain = !TR || own_i0 >= n_t ? n_t : max(own_i0 - kLead + 1, 0);
   // The same barriers on every wavefront: one after the prologue and one
   // after each step but the last.
   if (idle) {
-    for (int32_t i = 0; i + 1 < n_t; ++i) {
+    int32_t i = 0;
+    for (; i + 1 < n_plain; ++i) {
+      step_loads(i, std::false_type{});
+      end_step(i);
+    }
+    for (; i + 1 < n_t; ++i) {
       own_write(i, i & (NST - 1));
-      step_loads(i);
+      step_loads(i, tr);
       end_step(i);
     }
     own_write(n_t - 1, (n_t - 1) & (NST - 1));
@@ -792,7 +803,7 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
       return;
     }
     own_write(0, 0);
-    step_loads(0);
+    step_loads(0, tr);
     tile(nh_c, 0, true, false, 0);
     end_step(0);
     // NST steps per iteration, so that each tile's stage (i mod NST, with
@@ -800,25 +811,36 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
     // fold into the instructions' offsets
     int32_t i = 1;
     // each step reads block 0's K operands before issuing its loads, so that
-    // their LDS latency overlaps the load addresses.  Tiles with own rows to
-    // store go to the loop below.
+    // their LDS latency overlaps the load addresses.  Three copies: steps
+    // before the own rows (no test in the loads), steps that may load own
+    // rows, and steps that also store them (a workgroup of query group 0,
+    // from the first tile with own rows to the end).
     const int32_t n_fast = min(n_t, own_i0 < own_i1 ? own_i0 + 1 : n_t);
     h8 kf0[4];
-    for (; i + NST < n_fast; i += NST) {
+    auto fast_steps = [&](auto tr_c, auto own_c, int32_t n) __attribute__((always_inline)) {
+      for (; i + NST < n; i += NST) {
 #pragma unroll
-      for (int k = 0; k < NST; ++k) {
-        constexpr int kStage0 = 1;  // i = 1 mod NST here
-        const int st = (kStage0 + k) & (NST - 1);
-        read_k(lds_k[st], 0, kf0);
-        __builtin_amdgcn_sched_barrier(0);
-        step_loads(i + k);
-        tile(nh_c, i + k, false, false, st, kf0);
-        end_step(i + k);
+        for (int k = 0; k < NST; ++k) {
+          constexpr int kStage0 = 1;  // i = 1 mod NST here
+          const int st = (kStage0 + k) & (NST - 1);
+          read_k(lds_k[st], 0, kf0);
+          __builtin_amdgcn_sched_barrier(0);
+          step_loads(i + k, tr_c);
+          tile(nh_c, i + k, false, false, st, kf0);
+          if constexpr (decltype(own_c)::value) {
+            __builtin_amdgcn_sched_barrier(0);
+            own_write(i + k, st);
+          }
+          end_step(i + k);
+        }
       }
-    }
+    };
+    fast_steps(std::false_type{}, std::false_type{}, min(n_plain, n_fast));
+    if (TR) fast_steps(tr, std::false_type{}, n_fast);
+    if (TR && own_i0 < own_i1) fast_steps(tr, std::true_type{}, n_t);
     for (; i + 1 < n_t; ++i) {
       own_write(i, i & (NST - 1));
-      step_loads(i);
+      step_loads(i, tr);
       tile(nh_c, i, false, false, i & (NST - 1));
       end_step(i);
     }
