@@ -433,17 +433,22 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
     const int32_t key = (t_begin + i) * 64 + r;
     if (key < a.tr_start || key >= a.kv_len) return;
     const uint32_t code = lds_code[i & (NCODE - 1)][r];
-    const bool special = (code >> 31) != 0;
-    // the pools are the cache's own device buffers, read-only to every other
-    // launch form; only this store writes through them
-    char* kd = static_cast<char*>(const_cast<void*>(special ? a.special_pool : a.patch_pool)) +
-               (code & 0x7fffffffu) + head * D * 2;
-    char* vd = kd + (special ? a.vstride_special : a.vstride_patch);
     const int c0 = lc;
     const uint4 k0 = *reinterpret_cast<const uint4*>(&lds_k[stage][r * LS + ((c0 ^ k_swz(r)) * 8)]);
     const uint4 v0 = *reinterpret_cast<const uint4*>(&lds_v[stage][r * LS + ((c0 ^ v_swz(r)) * 8)]);
-    reinterpret_cast<uint4*>(kd)[c0] = k0;
-    reinterpret_cast<uint4*>(vd)[c0] = v0;
+    // 32-bit offsets from the pool's (scalar) base: row offsets and V strides
+    // are below 2^31 each.  The pools are the cache's own device buffers,
+    // read-only to every other launch form; only this store writes through them.
+    const uint32_t off = (code & 0x7fffffffu) + uint32_t(head * D * 2 + c0 * 16);
+    if (code >> 31) {
+      char* const base = static_cast<char*>(const_cast<void*>(a.special_pool));
+      *reinterpret_cast<uint4*>(base + off) = k0;
+      *reinterpret_cast<uint4*>(base + (off + uint32_t(a.vstride_special))) = v0;
+    } else {
+      char* const base = static_cast<char*>(const_cast<void*>(a.patch_pool));
+      *reinterpret_cast<uint4*>(base + off) = k0;
+      *reinterpret_cast<uint4*>(base + (off + uint32_t(a.vstride_patch))) = v0;
+    }
   };
 
   // K operand: row kb*32 + l32, chunk 2ks + hh (swizzle depends on l32 only).
