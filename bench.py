@@ -2,9 +2,9 @@
 
 One step = one new frame through all 24 blocks: per block, one
 lbm_append_run (block 0 also reserves, plans -- one small table upload and
-the row-table kernel -- and evicts): one launch of paged attention (HIP,
-bf16 MFMA) whose extra workgroups copy the block's K/V rows into their
-pages.  Shapes: 1369 patch + 6 special tokens per frame, 16 heads x 64,
+the row-table kernel -- and evicts): the append kernel (the block's K/V rows
+into their pages), then paged attention (HIP, bf16 MFMA) and the split merge.
+Shapes: 1369 patch + 6 special tokens per frame, 16 heads x 64,
 scale_frames 8, sliding_window 64, bf16 unit-normal inputs.
 
 Setup (untimed): the 8-frame first step and 64 single frames (F = 72, the
@@ -19,9 +19,10 @@ only, and the last 20 frames of the 10,000-frame 4-block stream (F =
 9981..10000, 38% of the keys special), reached the same way.
 
 Printed: one JSON line with frames/s (value), the attention kernel's roofline
-(algorithmic FLOPs per launch / launch time from HIP events on the launch
-stream, against the bf16 dense MFMA peak), the windows, and the CPU oracle
-timed on a bounded sample of the same step.
+(algorithmic FLOPs per call / call time from HIP events on the launch stream
+around one lbm_append_run -- append, attention and merge -- against the bf16
+dense MFMA peak), the windows, and the CPU oracle timed on a bounded sample of
+the same step.
 """
 from __future__ import annotations
 
@@ -88,6 +89,7 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic__attn_d64_kernel_bf16__
 KERNEL_SOURCES = ["paged_kv_cache_312_amd/csrc/hip/attn16.hip",
                   "paged_kv_cache_312_amd/csrc/hip/attn_common.h",
                   "paged_kv_cache_312_amd/csrc/hip/merge.hip",
+                  "paged_kv_cache_312_amd/csrc/hip/append.hip",
                   "paged_kv_cache_312_amd/csrc/hip/kernels.h",
                   "paged_kv_cache_312_amd/csrc/hip/api.hip"]
 APPEND_SOURCES = ["paged_kv_cache_312_amd/csrc/hip/append.hip",
@@ -96,7 +98,7 @@ COPY_BYTES = 1 << 30
 
 
 def kernel_source_hash(root: str = ROOT, sources=None) -> str:
-    """Hash of the attention and merge sources (or of ``sources``) with
+    """Hash of the append, attention and merge sources (or of ``sources``) with
     comments and blank space removed (a comment edit does not change the
     kernel)."""
     import hashlib
@@ -120,8 +122,9 @@ def _traffic_record():
 
 
 def recorded_traffic():
-    """Bytes per lbm_run from the traffic record, or None if it is missing or
-    was measured on other kernel sources."""
+    """HBM bytes per lbm_append_run (append, attention and merge) from the
+    traffic record, or None if it is missing or was measured on other kernel
+    sources."""
     rec = _traffic_record()
     if rec is None or rec.get("kernel_source_hash") != kernel_source_hash():
         return None
@@ -169,29 +172,37 @@ def pmc_summary(fetch_dir, write_dir):
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = load(d, counter)
         ids = sorted(per)
-        # steady state only: the two timed steps (48 fused launches at F =
-        # 73, 74), not the append-timing step after them (24 launches without
-        # the append) nor the first step and the fill steps (other shapes)
-        # (the counter runs time bf16 only, so every attention instance is a
-        # bf16 one; rocprofv3 may print the skip-append form's name without
-        # its template arguments)
+        # steady state only: the two timed steps (48 calls at F = 73, 74:
+        # append, attention, merge each), not the append-timing step after
+        # them (24 appends, then 24 attention launches) nor the first step and
+        # the fill steps (other shapes) (the counter runs time bf16 only, so
+        # every attention instance is a bf16 one)
         attn = [per[i][1] for i in ids if "attn_d64_kernel" in per[i][0]][-72:-24]
         merge = [per[i][1] for i in ids if bf16_kernel(per[i][0], "merge_kernel")][-72:-24]
-        # the separate single-frame appends of the append-timing step
-        app = [per[i][1] for i in ids if "append_scatter_kernel" in per[i][0]][-23:]
+        apps = [per[i][1] for i in ids if "append_scatter_kernel" in per[i][0]]
+        app_run = apps[-72:-24]
+        # the single-frame appends of blocks 1..23 of the append-timing step
+        app = apps[-23:]
         copy = [per[i][1] for i in ids if "elementwise" in per[i][0]][-3:]
         if not attn or len(copy) < 3:
             raise SystemExit(f"{counter}: attention or calibration dispatches missing")
         out[counter] = {"attn_kib": statistics.mean(attn),
                         "merge_kib": statistics.mean(merge) if merge else 0.0,
                         "merges_per_attn": len(merge) / len(attn),
+                        "run_append_kib": statistics.mean(app_run) if app_run else 0.0,
+                        "appends_per_attn": len(app_run) / len(attn),
                         "append_kib": statistics.mean(app) if app else None,
                         "copy_kib": statistics.mean(copy)}
     f, w = out["FETCH_SIZE"], out["WRITE_SIZE"]
     f_scale = COPY_BYTES / (f["copy_kib"] * 1024.0)
     w_scale = COPY_BYTES / (w["copy_kib"] * 1024.0)
-    fetch_b = (f["attn_kib"] + f["merge_kib"] * f["merges_per_attn"]) * 1024.0 * f_scale
-    write_b = (w["attn_kib"] + w["merge_kib"] * w["merges_per_attn"]) * 1024.0 * w_scale
+
+    def per_call(x):
+        return (x["attn_kib"] + x["merge_kib"] * x["merges_per_attn"]
+                + x["run_append_kib"] * x["appends_per_attn"]) * 1024.0
+
+    fetch_b = per_call(f) * f_scale
+    write_b = per_call(w) * w_scale
     rec = {"kernel_source_hash": kernel_source_hash(),
            "hbm_bytes_per_lbm_run": round(fetch_b + write_b),
            "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
@@ -205,8 +216,8 @@ def pmc_summary(fetch_dir, write_dir):
                    append_fetch_bytes=round(a_fetch), append_write_bytes=round(a_write))
     os.makedirs(os.path.dirname(TRAFFIC_RECORD), exist_ok=True)
     with open(TRAFFIC_RECORD, "w") as fh:
-        fh.write("HBM traffic of one lbm_append_run (attention with the block's append, + "
-                 "merge) and of one separate single-frame append, 24-block ViT-L step; written by "
+        fh.write("HBM traffic of one lbm_append_run (the block's append, attention, merge) and "
+                 "of one single-frame append, 24-block ViT-L step; written by "
                  "'bench.py --pmc-summary' from two rocprofv3 --pmc runs of 'bench.py --steps 2 "
                  "--warmup 0 --no-cpu-baseline --no-variants --no-windows --calibrate-copy' (FETCH_SIZE, "
                  "then WRITE_SIZE)\n")
@@ -220,7 +231,7 @@ class Stream:
     single frames drawn from N_INPUT_SETS seeded input sets per block (resident
     in HBM, cycled).  A frame step appends every block's rows, evicts and
     plans once (at block 0) and runs attention per block: with ``fused``, one
-    lbm_append_run per block (append and attention in one launch), else
+    lbm_append_run per block (append and attention in one call), else
     lbm_append_frame, lbm_evict_frames, lbm_plan and lbm_run.  A fast-forward
     step (``run=False``) appends and evicts only."""
 
@@ -292,11 +303,12 @@ class Stream:
 
     def window(self, steps):
         """Time ``steps`` frame steps: wall clock over the whole steps, and HIP
-        events on the launch stream around one attention launch per step
-        (block i mod B of step i, or 1 + i mod (B-1) with fused calls: every
-        block's launch has the same shape within a step, and an event pair at
-        every launch would itself add ~6 us of queue work per event to the
-        steps being timed)."""
+        events on the launch stream around one call per step (lbm_append_run:
+        append, attention, merge; separate calls: lbm_run's attention and
+        merge) (block i mod B of step i, or 1 + i mod (B-1) with
+        lbm_append_run, whose block 0 also plans: every block's launch has
+        the same shape within a step, and an event pair at every launch would
+        itself add ~6 us of queue work per event to the steps being timed)."""
         import statistics
 
         import torch
@@ -624,17 +636,16 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(),
-                     "kernel": "attn_d64_kernel<__bf16> (+ merge_kernel): one lbm_append_run "
-                               "(attention whose query group 0 also stores the block's frame "
-                               "rows it stages into their pages)",
+                     "kernel": "attn_d64_kernel<__bf16> (+ merge_kernel, after the block's "
+                               "append_scatter_kernel): one lbm_append_run",
                      "avg_launch_ms": round(avg_launch_ms, 4),
                      "flops_per_launch_avg": flops / n_launch},
-        # the timed steps carry each block's append inside its attention
-        # launch (lbm_append_run); the separate append kernel (lbm_append_frame)
-        # is timed on one more step for reference, and the whole step made of
-        # separate calls is a variant below
-        "append": {"mode": "stored by the attention launch (query group 0, from the rows it stages)",
-                   "separate_kernel": {
+        # each timed call runs the block's append kernel before its attention
+        # (lbm_append_run); the append kernel's rate is timed on one more step,
+        # its 23 appends back to back between one event pair, and the whole
+        # step made of separate calls is a variant below
+        "append": {"mode": "append kernel before the attention launch, in the same call",
+                   "kernel": {
                        "bound": "hbm", "achieved": round(append_gbps, 1), "peak": PEAK_HBM_GBPS,
                        "unit": "GB/s", "frac": round(append_gbps / PEAK_HBM_GBPS, 4),
                        "traffic": recorded_append_traffic(),
@@ -651,8 +662,8 @@ def main():
             "avg_launch_ms": round(sk["avg_launch_ms"], 4)}}
     if not args.no_variants:
         # the same stream made of separate calls per block (lbm_append_frame,
-        # then lbm_run; evict and plan once): the append kernel's launches are
-        # back in the step
+        # then lbm_run; evict and plan once): the same kernels, and the events
+        # bracket lbm_run alone (attention and merge, not the append)
         v = measure_stream(cfg, dev, args.variant_steps, args.warmup, args.splits, fused=False)
         result.setdefault("variants", {})["separate_calls_bf16"] = {
             "value": round(v["fps"], 3), "unit": "frames/s", "steps": args.variant_steps,

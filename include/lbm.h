@@ -204,22 +204,20 @@ lbm_status lbm_plan_transient(lbm_cache* cache, int32_t num_q_tokens, int32_t nu
 lbm_status lbm_run_transient(lbm_cache* cache, int32_t block_idx, const void* q, const void* k,
                              const void* v, void* out, int32_t num_q_tokens, void* hip_stream);
 
-/* One block's append and attention of a frame step in one launch: the append
+/* One block's append and attention of a frame step in one call: the append
  * of [P2] "Appending New Frames" and the run of [P4] "Plan-Run Execution
  * Workflow", for callers that make both calls per block back to back.
  * k, v: device [num_frames, P + S, H, D] as for lbm_append_frame; q, out:
  * device [num_q_tokens, H, D] as for lbm_run.  block_idx 0 opens the step: it
  * reserves the pages (as lbm_append_frame), plans (num_q_tokens queries), and
  * evicts (as lbm_evict_frames; the ids are not reported).  Every block's call
- * then enqueues one attention launch that reads the step's own rows from k, v
- * (as lbm_run_transient does) and the rest of the visible set from the pages,
- * and stores the own rows into the reserved pages: in the 16-bit kernels the
- * workgroups of query group 0 store the rows they stage, from LDS; the fp32
- * kernel's launch carries extra workgroups that copy them.  The result is the
- * same attention as lbm_append_frame + lbm_plan + lbm_run (the keys taken in
- * another order).  Blocks 1..num_blocks-1 follow
+ * then enqueues the append kernel (the rows into the reserved pages) and the
+ * attention over the visible set, the step's own rows read back from those
+ * pages (and the merge).  The result is the same attention as
+ * lbm_append_frame + lbm_plan + lbm_run (the keys taken in another order).
+ * Blocks 1..num_blocks-1 follow
  * block 0 in the same step, each once, with the same num_frames and
- * num_q_tokens.  k and v must stay unchanged until the launch has run.
+ * num_q_tokens.  k and v must stay unchanged until the append has run.
  * Requires num_frames <= sliding_window (every frame of the step stays
  * visible).  Errors: INVALID_ARG, BAD_STATE (block out of order, the open step
  * opened by lbm_append_frame), OUT_OF_PAGES (nothing changes); a plan refused

@@ -333,7 +333,7 @@ class PagedKVCache:
         return out
 
     def append_run(self, block_idx: int, q, k, v, out=None, stream=None):
-        """One block's append and attention of a frame step in one launch
+        """One block's append and attention of a frame step in one call
         (block 0 also reserves, plans for q's rows and evicts); returns out."""
         T = self.cfg.patches_per_frame + self.cfg.special_per_frame
         nf = k.shape[0] // T

@@ -205,8 +205,7 @@ AttnArgs base_args(const lbm_config& c, const void* q, void* out, int32_t nq, co
 // c's head_dim and dtype, all with or all without own rows), then the merge
 // of every stream whose key range is split.
 lbm_status launch_attention_batch(const lbm_config& c, AttnArgs* as, int32_t n, int32_t splits,
-                                  hipStream_t st, const FusedAppend* app = nullptr,
-                                  int32_t groups = 0) {
+                                  hipStream_t st, int32_t groups = 0) {
   BatchArgs b;
   std::memset(&b, 0, sizeof(b));
   b.n = n;
@@ -217,10 +216,6 @@ lbm_status launch_attention_batch(const lbm_config& c, AttnArgs* as, int32_t n, 
   }
   b.total_items = b.item_start[n];
   b.items_per_xcd = (b.total_items + 7) / 8;
-  if (app) {
-    b.app = *app;
-    b.app.wg0 = 8 * b.items_per_xcd;
-  }
   const bool own = as[0].tr_start < as[0].kv_len;
   hipError_t e = c.dtype == LBM_F32 ? launch_attn_f32(b, c.head_dim, own, st)
                                     : launch_attn16(b, c.head_dim, c.dtype == LBM_F16, own, st);
@@ -235,8 +230,8 @@ lbm_status launch_attention_batch(const lbm_config& c, AttnArgs* as, int32_t n, 
 }
 
 lbm_status launch_attention(const lbm_config& c, AttnArgs* a, int32_t splits, hipStream_t st,
-                            const FusedAppend* app = nullptr, int32_t groups = 0) {
-  return launch_attention_batch(c, a, 1, splits, st, app, groups);
+                            int32_t groups = 0) {
+  return launch_attention_batch(c, a, 1, splits, st, groups);
 }
 
 // the planner's query groups are chosen for the 16-bit kernel only
@@ -357,7 +352,7 @@ lbm_status paged_attention_impl(const lbm_config* cfg, const void* q, void* out,
                                    attn_occupancy(cfg->dtype, cfg->head_dim), cap,
                                    cfg->num_splits, kernel_rows_per_wg(cfg->dtype),
                                    groups_out(cfg->dtype, &groups));
-  return launch_attention(*cfg, &a, ns < 1 ? 1 : ns, stream, nullptr, groups);
+  return launch_attention(*cfg, &a, ns < 1 ? 1 : ns, stream, groups);
 }
 
 }  // namespace
@@ -418,7 +413,7 @@ lbm_status lbm_cache_create(const lbm_config* cfg, void* const* patch_pools,
   c->wg_per_cu = attn_occupancy(cfg->dtype, cfg->head_dim);
 
   // staging = workspace [desc_off, special ids end): the step descriptor (a
-  // fused append's pages), then the tables
+  // graph step's), then the tables
   c->staging_bytes = c->ws.special_ids_off - c->ws.desc_off +
                      sizeof(int32_t) * size_t(std::max(1, cfg->max_special_pages));
   for (int i = 0; i < 2; ++i) {
@@ -470,6 +465,31 @@ lbm_status lbm_cache_seed_free_lists(lbm_cache* c, const int32_t* patch_order, i
   return st;
 }
 
+// The append kernel over block_idx's rows of the open step, into the pages
+// block 0's append reserved (the bookkeeping's write map).
+static lbm_status launch_block_append(const lbm_cache* c, int32_t block_idx, const void* k,
+                                      const void* v, hipStream_t stream) {
+  const WriteMap& wm = c->bk.write_map();
+  AppendArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.k = static_cast<const uint4*>(k);
+  a.v = static_cast<const uint4*>(v);
+  a.patch_pool = static_cast<uint4*>(c->patch_pools[size_t(block_idx)]);
+  a.special_pool = static_cast<uint4*>(c->special_pools[size_t(block_idx)]);
+  a.P = c->cfg.patches_per_frame;
+  a.S = c->cfg.special_per_frame;
+  a.T = a.P + a.S;
+  a.SPS = c->cfg.special_page_size;
+  a.rc = int32_t(size_t(c->cfg.num_heads) * c->cfg.head_dim * dtype_size(c->cfg.dtype) / 16);
+  a.st0 = wm.st0;
+  a.sp_first = wm.sp_first;
+  for (int32_t f = 0; f < wm.nf; ++f) a.patch_pages[f] = wm.patch_pages[f];
+  for (int32_t i = 0; i < wm.n_sp; ++i) a.spages[i] = wm.spages[i];
+  const hipError_t e = launch_append(a, wm.nf, stream);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return LBM_OK;
+}
+
 lbm_status lbm_append_frame(lbm_cache* c, int32_t block_idx, const void* k, const void* v,
                             int32_t num_frames, void* hip_stream) {
   clear_error();
@@ -501,24 +521,8 @@ lbm_status lbm_append_frame(lbm_cache* c, int32_t block_idx, const void* k, cons
       return fail(LBM_ERR_INVALID_ARG, "block %d appends %d frames, block 0 appended %d",
                   block_idx, num_frames, c->step_nf);
   }
-  const WriteMap& wm = c->bk.write_map();
-  AppendArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.k = static_cast<const uint4*>(k);
-  a.v = static_cast<const uint4*>(v);
-  a.patch_pool = static_cast<uint4*>(c->patch_pools[size_t(block_idx)]);
-  a.special_pool = static_cast<uint4*>(c->special_pools[size_t(block_idx)]);
-  a.P = c->cfg.patches_per_frame;
-  a.S = c->cfg.special_per_frame;
-  a.T = a.P + a.S;
-  a.SPS = c->cfg.special_page_size;
-  a.rc = int32_t(size_t(c->cfg.num_heads) * c->cfg.head_dim * dtype_size(c->cfg.dtype) / 16);
-  a.st0 = wm.st0;
-  a.sp_first = wm.sp_first;
-  for (int32_t f = 0; f < wm.nf; ++f) a.patch_pages[f] = wm.patch_pages[f];
-  for (int32_t i = 0; i < wm.n_sp; ++i) a.spages[i] = wm.spages[i];
-  const hipError_t e = launch_append(a, wm.nf, static_cast<hipStream_t>(hip_stream));
-  if (e != hipSuccess) return hip_fail(e, "append launch");
+  st = launch_block_append(c, block_idx, k, v, static_cast<hipStream_t>(hip_stream));
+  if (st != LBM_OK) return st;
   c->appended[size_t(block_idx)] = 1;
   return LBM_OK;
 }
@@ -553,8 +557,9 @@ namespace {
 // special stream).  fused_nf > 0: the plan of lbm_append_run for the open
 // step of fused_nf frames: the visible set without the step's own rows (its
 // patch pages are the last fused_nf visible pages, its specials the last
-// fused_nf * S special tokens), which the attention reads from the caller's
-// rows instead; the step descriptor carries the pages the launches write.
+// fused_nf * S special tokens), then those rows frame by frame at their
+// destinations, where each block's append writes them before the block's
+// attention reads them.
 lbm_status plan_impl(lbm_cache* c, int32_t num_q_tokens, int32_t own, void* hip_stream,
                      int32_t fused_nf = 0) {
   if (num_q_tokens < 1 || num_q_tokens > c->cfg.max_q_tokens)
@@ -565,7 +570,6 @@ lbm_status plan_impl(lbm_cache* c, int32_t num_q_tokens, int32_t own, void* hip_
   if (p.kv_len < 1) return fail(LBM_ERR_BAD_STATE, "no visible tokens");
   std::vector<int32_t> pp;
   c->bk.visible_patch_pages(&pp);
-  StepDesc d;
   if (fused_nf > 0) {
     const WriteMap& wm = c->bk.write_map();
     const int32_t T = c->cfg.patches_per_frame + c->cfg.special_per_frame;
@@ -577,14 +581,10 @@ lbm_status plan_impl(lbm_cache* c, int32_t num_q_tokens, int32_t own, void* hip_
     own = fused_nf * T;
     p.patch_tokens -= fused_nf * c->cfg.patches_per_frame;
     p.kv_len -= own;
-    d.st0 = wm.st0;
-    d.sp_first = wm.sp_first;
-    for (int32_t f = 0; f < wm.nf; ++f) d.patch_pages[f] = wm.patch_pages[f];
-    for (int32_t j = 0; j < wm.n_sp; ++j) d.spages[j] = wm.spages[j];
   }
 
-  // stage [desc | patch ids | pad | special ids] exactly as laid out in the
-  // workspace; the descriptor travels only with a fused plan
+  // stage [patch ids | pad | special ids] exactly as laid out in the
+  // workspace (the step descriptor before them is the graph step's)
   const int i = c->staging_next;
   if (c->staging_pending[i]) {
     const hipError_t e = hipEventSynchronize(c->staging_ev[i]);
@@ -594,11 +594,10 @@ lbm_status plan_impl(lbm_cache* c, int32_t num_q_tokens, int32_t own, void* hip_
   char* stg = reinterpret_cast<char*>(c->staging[i]);
   const size_t pp_off = c->ws.patch_ids_off - c->ws.desc_off;
   const size_t sp_off = c->ws.special_ids_off - c->ws.desc_off;
-  if (fused_nf > 0) std::memcpy(stg, &d, sizeof(d));
   std::memcpy(stg + pp_off, pp.data(), sizeof(int32_t) * pp.size());
   const std::vector<int32_t>& sp = c->bk.special_pages();
   if (!sp.empty()) std::memcpy(stg + sp_off, sp.data(), sizeof(int32_t) * sp.size());
-  const size_t from = fused_nf > 0 ? 0 : pp_off;
+  const size_t from = pp_off;
   const size_t bytes = sp_off + sizeof(int32_t) * sp.size() - from;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   hipError_t e = hipMemcpyAsync(c->workspace + c->ws.desc_off + from, stg + from, bytes,
@@ -684,7 +683,7 @@ lbm_status lbm_run(lbm_cache* c, int32_t block_idx, const void* q, void* out,
   a.kv_len = c->plan.kv_len;
   a.tr_start = a.kv_len;
   return launch_attention(c->cfg, &a, c->plan_splits, static_cast<hipStream_t>(hip_stream),
-                          nullptr, c->plan_groups);
+                          c->plan_groups);
 }
 
 lbm_status lbm_run_transient(lbm_cache* c, int32_t block_idx, const void* q, const void* k,
@@ -712,7 +711,7 @@ lbm_status lbm_run_transient(lbm_cache* c, int32_t block_idx, const void* q, con
   a.tk = k;
   a.tv = v;
   return launch_attention(c->cfg, &a, c->plan_splits, static_cast<hipStream_t>(hip_stream),
-                          nullptr, c->plan_groups);
+                          c->plan_groups);
 }
 
 lbm_status lbm_append_run(lbm_cache* c, int32_t block_idx, const void* q, const void* k,
@@ -782,37 +781,20 @@ lbm_status lbm_append_run(lbm_cache* c, int32_t block_idx, const void* q, const 
       return fail(LBM_ERR_BAD_STATE, "run with %d queries, plan made for %d", num_q_tokens,
                   c->plan_q);
   }
+  // The block's rows into the step's pages, then the attention over the
+  // visible set and those rows, read back from the pools (the plan's row
+  // table holds the rows' destinations at the own positions): two launches
+  // back to back, which measured faster than one attention launch that reads
+  // the rows from k / v and stores them from the tiles it stages.
+  st = launch_block_append(c, block_idx, k, v, s);
+  if (st != LBM_OK) return st;
   AttnArgs a = base_args(c->cfg, q, out, num_q_tokens, c->patch_pools[size_t(block_idx)],
                          c->special_pools[size_t(block_idx)],
                          reinterpret_cast<const uint32_t*>(c->workspace + c->ws.rowtab_off),
                          c->workspace, c->ws);
-  a.tr_start = c->plan.kv_len;
   a.kv_len = c->plan.kv_len + c->plan_own;
-  a.tk = k;
-  a.tv = v;
-  FusedAppend f;
-  std::memset(&f, 0, sizeof(f));
-  f.k = static_cast<const uint4*>(k);
-  f.v = static_cast<const uint4*>(v);
-  f.patch_pool = static_cast<uint4*>(c->patch_pools[size_t(block_idx)]);
-  f.special_pool = static_cast<uint4*>(c->special_pools[size_t(block_idx)]);
-  f.desc = reinterpret_cast<const StepDesc*>(c->workspace + c->ws.desc_off);
-  f.rows = num_frames * T;
-  f.T = T;
-  f.P = c->cfg.patches_per_frame;
-  f.S = c->cfg.special_per_frame;
-  f.SPS = c->cfg.special_page_size;
-  f.rc = int32_t(size_t(c->cfg.num_heads) * c->cfg.head_dim * dtype_size(c->cfg.dtype) / 16);
-  if (c->cfg.dtype == LBM_F32) {
-    // the fp32 kernel: extra workgroups copy the rows, about 16 rows of K or
-    // V per workgroup, at most 256 workgroups
-    f.wgs = std::max(1, std::min(256, (2 * f.rows + 15) / 16));
-  } else {
-    // the 16-bit kernels: query group 0 of each key range stores the rows it
-    // stages (their destinations are the row table's own codes)
-    a.own_store = 1;
-  }
-  st = launch_attention(c->cfg, &a, c->plan_splits, s, &f, c->plan_groups);
+  a.tr_start = a.kv_len;
+  st = launch_attention(c->cfg, &a, c->plan_splits, s, c->plan_groups);
   if (st != LBM_OK) return st;
   c->appended[size_t(block_idx)] = 1;
   return LBM_OK;
@@ -995,7 +977,7 @@ lbm_status graph_capture(lbm_graph* g, int i, const void* const* k, const void* 
     a.kv_len = g->ns * kKeysPerTile;
     a.tr_start = a.kv_len;
     a.desc = desc;
-    st = launch_attention(cfg, &a, g->ns, g->cap_stream, nullptr, g->groups);
+    st = launch_attention(cfg, &a, g->ns, g->cap_stream, g->groups);
   }
   hipGraph_t graph = nullptr;
   e = hipStreamEndCapture(g->cap_stream, &graph);

@@ -224,10 +224,10 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
   }
   // item -> (query group, head, key range); the groups sharing a key range
   // are consecutive items, so they run side by side on one L2.  A head's
-  // key ranges go out last first: the last range holds the frame's own rows,
-  // whose query group 0 stores them in a fused step, and dispatched early its
-  // workgroups have slack (a slot whose first workgroup ends late takes no
-  // second one).
+  // key ranges go out last first: the last range holds a skip-append step's
+  // own rows, read from the caller's buffers, and dispatched early its
+  // workgroups have slack when a launch takes more than one round (a slot
+  // whose first workgroup ends late takes no second one).
   const int32_t qt = item % a.n_qt;
   const int32_t grp = item / a.n_qt;
   const int32_t head = grp / a.num_splits;
@@ -349,8 +349,8 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
     const char* base = special ? col_base[1][v] : col_base[0][v];
     return base + (code & 0x7fffffffu);
   };
-  // K and V of tile position x into stage x mod NST.  Skip-append step (and
-  // a fused append): keys in [tr_start, kv_len) come from the frame's own rows
+  // K and V of tile position x into stage x mod NST.  Skip-append step: keys
+  // in [tr_start, kv_len) come from the frame's own rows
   // (the row table holds position 0's code there), and so does the padding
   // past kv_len; the test is uniform per tile, and only the step's last tiles
   // take that branch.  tr_c: whether the test is made (steps that load no
@@ -413,43 +413,8 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
     code_nx = codes_of(i + 1 + kLead);
     barrier();
   };
-  // lbm_append_run: the workgroups of query group 0 store the frame's own
-  // rows of their tiles (staged in LDS from the caller's rows) into the
-  // pages the step reserved, whose codes the row table holds at the own
-  // positions; the other groups only read them.  In step i (at its start,
-  // or at its end in the unrolled loop), while position i's stage is
-  // resident: wavefront w stores rows 8w .. 8w+7 of the tile, lane l row
-  // 8w + l/8, chunk l%8 of this head's K and V (the row and chunk it
-  // loaded).  The stores count in the vector-memory counter beside the
-  // loads; loads still complete in order, so each step's wait for its oldest
-  // loads stays sufficient.
-  const bool own_store = TR && a.own_store != 0 && qt == 0;
-  // the steps whose tiles hold own rows: [own_i0, own_i1), empty without
+  // the first step whose tile holds own rows (skip-append step)
   const int32_t own_i0 = a.tr_start / 64 - t_begin;
-  const int32_t own_i1 = own_store ? (a.kv_len + 63) / 64 - t_begin : own_i0;
-  auto own_write = [&](int32_t i, int stage) __attribute__((always_inline)) {
-    if (!TR || i < own_i0 || i >= own_i1) return;
-    const int r = lp;
-    const int32_t key = (t_begin + i) * 64 + r;
-    if (key < a.tr_start || key >= a.kv_len) return;
-    const uint32_t code = lds_code[i & (NCODE - 1)][r];
-    const int c0 = lc;
-    const uint4 k0 = *reinterpret_cast<const uint4*>(&lds_k[stage][r * LS + ((c0 ^ k_swz(r)) * 8)]);
-    const uint4 v0 = *reinterpret_cast<const uint4*>(&lds_v[stage][r * LS + ((c0 ^ v_swz(r)) * 8)]);
-    // 32-bit offsets from the pool's (scalar) base: row offsets and V strides
-    // are below 2^31 each.  The pools are the cache's own device buffers,
-    // read-only to every other launch form; only this store writes through them.
-    const uint32_t off = (code & 0x7fffffffu) + uint32_t(head * D * 2 + c0 * 16);
-    if (code >> 31) {
-      char* const base = static_cast<char*>(const_cast<void*>(a.special_pool));
-      *reinterpret_cast<uint4*>(base + off) = k0;
-      *reinterpret_cast<uint4*>(base + (off + uint32_t(a.vstride_special))) = v0;
-    } else {
-      char* const base = static_cast<char*>(const_cast<void*>(a.patch_pool));
-      *reinterpret_cast<uint4*>(base + off) = k0;
-      *reinterpret_cast<uint4*>(base + (off + uint32_t(a.vstride_patch))) = v0;
-    }
-  };
 
   // K operand: row kb*32 + l32, chunk 2ks + hh (swizzle depends on l32 only).
   // V transpose read: within each 16-lane group g, lane s points at row
@@ -780,8 +745,8 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
   barrier();
   code_nx = codes_of(kLead);
 
-  // Steps before n_plain - 1 neither load (kLead ahead) nor store own rows:
-  // they take the loads without the test for them.
+  // Steps before n_plain - 1 load no own row (kLead ahead): they take the
+  // loads without the test for it.
   const int32_t n_plain = !TR || own_i0 >= n_t ? n_t : max(own_i0 - kLead + 1, 0);
   // The same barriers on every wavefront: one after the prologue and one
   // after each step but the last.
@@ -792,22 +757,18 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
       end_step(i);
     }
     for (; i + 1 < n_t; ++i) {
-      own_write(i, i & (NST - 1));
       step_loads(i, tr);
       end_step(i);
     }
-    own_write(n_t - 1, (n_t - 1) & (NST - 1));
     LBM_WAIT_VMCNT(0);
     return;
   }
   // NH halves hold rows: a wavefront with one half runs that half only
   auto steps = [&](auto nh_c) __attribute__((always_inline)) {
     if (n_t == 1) {
-      own_write(0, 0);
       tile(nh_c, 0, true, true, 0);
       return;
     }
-    own_write(0, 0);
     step_loads(0, tr);
     tile(nh_c, 0, true, false, 0);
     end_step(0);
@@ -816,13 +777,11 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
     // fold into the instructions' offsets
     int32_t i = 1;
     // each step reads block 0's K operands before issuing its loads, so that
-    // their LDS latency overlaps the load addresses.  Three copies: steps
-    // before the own rows (no test in the loads), steps that may load own
-    // rows, and steps that also store them (a workgroup of query group 0,
-    // from the first tile with own rows to the end).
-    const int32_t n_fast = min(n_t, own_i0 < own_i1 ? own_i0 + 1 : n_t);
+    // their LDS latency overlaps the load addresses.  Two copies on a
+    // skip-append step: the steps before the own rows (no test in the loads)
+    // and the rest.
     h8 kf0[4];
-    auto fast_steps = [&](auto tr_c, auto own_c, int32_t n) __attribute__((always_inline)) {
+    auto fast_steps = [&](auto tr_c, int32_t n) __attribute__((always_inline)) {
       for (; i + NST < n; i += NST) {
 #pragma unroll
         for (int k = 0; k < NST; ++k) {
@@ -832,24 +791,17 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
           __builtin_amdgcn_sched_barrier(0);
           step_loads(i + k, tr_c);
           tile(nh_c, i + k, false, false, st, kf0);
-          if constexpr (decltype(own_c)::value) {
-            __builtin_amdgcn_sched_barrier(0);
-            own_write(i + k, st);
-          }
           end_step(i + k);
         }
       }
     };
-    fast_steps(std::false_type{}, std::false_type{}, min(n_plain, n_fast));
-    if (TR) fast_steps(tr, std::false_type{}, n_fast);
-    if (TR && own_i0 < own_i1) fast_steps(tr, std::true_type{}, n_t);
+    fast_steps(std::false_type{}, n_plain);
+    if (TR) fast_steps(tr, n_t);
     for (; i + 1 < n_t; ++i) {
-      own_write(i, i & (NST - 1));
       step_loads(i, tr);
       tile(nh_c, i, false, false, i & (NST - 1));
       end_step(i);
     }
-    own_write(n_t - 1, (n_t - 1) & (NST - 1));
     tile(nh_c, n_t - 1, false, true, (n_t - 1) & (NST - 1));
   };
   if (nh == 1)
@@ -902,9 +854,6 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
 hipError_t launch_attn16(const BatchArgs& b, int32_t head_dim, bool fp16, bool transient,
                          hipStream_t stream) {
   if (head_dim != 64) return hipErrorInvalidValue;
-  // (an append carried by the launch is stored by query group 0, own_store;
-  // the launch takes no extra workgroups)
-  if (b.app.wgs != 0) return hipErrorInvalidValue;
   const dim3 grid(8 * b.items_per_xcd), block(kThreads16);
   if (fp16 && transient)
     hipLaunchKernelGGL((attn_d64_kernel<_Float16, true>), grid, block, 0, stream, b);

@@ -49,51 +49,4 @@ __device__ __forceinline__ void kv_rows(const AttnArgs& a, uint32_t code, int32_
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Destination of chunk c of a fused append (see fused_append_wg).
-__device__ __forceinline__ uint4* fused_append_dst(const FusedAppend& f, int64_t c) {
-  const int32_t item = int32_t(c / f.rc);  // kv * rows + row
-  const int32_t cc = int32_t(c - int64_t(item) * f.rc);
-  const int32_t kv = item >= f.rows ? 1 : 0;
-  const int32_t row = item - kv * f.rows;
-  const int32_t fr = row / f.T;
-  const int32_t t = row - fr * f.T;
-  if (t < f.P) {
-    const size_t page = size_t(f.desc->patch_pages[fr]);
-    return f.patch_pool + ((page * 2 + kv) * f.P + t) * size_t(f.rc) + cc;
-  }
-  const int32_t g = f.desc->st0 + fr * f.S + (t - f.P);  // special token index in the stream
-  const int32_t pi = g / f.SPS;
-  const int32_t slot = g - pi * f.SPS;
-  const size_t page = size_t(f.desc->spages[pi - f.desc->sp_first]);
-  return f.special_pool + ((page * 2 + kv) * f.SPS + slot) * size_t(f.rc) + cc;
-}
-
-// Source of chunk c: K rows, then V rows.
-__device__ __forceinline__ const uint4* fused_append_src(const FusedAppend& f, int64_t c) {
-  const int64_t half = int64_t(f.rows) * f.rc;
-  return c < half ? f.k + c : f.v + (c - half);
-}
-
-// A workgroup of a fused append (see FusedAppend): workgroup w of the wgs
-// copies chunks [w * n / wgs, (w + 1) * n / wgs) of the step's n = 2 * rows *
-// rc 16-byte chunks (K rows, then V rows, each row rc chunks), four loads in
-// flight per lane before their stores.
-__device__ __forceinline__ void fused_append_wg(const FusedAppend& f, int32_t w) {
-  const int64_t n = int64_t(2) * f.rows * f.rc;
-  const int64_t c0 = n * w / f.wgs, c1 = n * (w + 1) / f.wgs;
-  const int64_t step = blockDim.x;
-  int64_t c = c0 + threadIdx.x;
-  for (; c + 3 * step < c1; c += 4 * step) {
-    const uint4 x0 = *fused_append_src(f, c);
-    const uint4 x1 = *fused_append_src(f, c + step);
-    const uint4 x2 = *fused_append_src(f, c + 2 * step);
-    const uint4 x3 = *fused_append_src(f, c + 3 * step);
-    *fused_append_dst(f, c) = x0;
-    *fused_append_dst(f, c + step) = x1;
-    *fused_append_dst(f, c + 2 * step) = x2;
-    *fused_append_dst(f, c + 3 * step) = x3;
-  }
-  for (; c < c1; c += step) *fused_append_dst(f, c) = *fused_append_src(f, c);
-}
-
 }  // namespace lbm

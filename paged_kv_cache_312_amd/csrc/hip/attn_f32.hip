@@ -32,11 +32,6 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const BatchArgs b) {
   __shared__ __attribute__((aligned(16))) float lds_k[2][64 * KS];
   __shared__ __attribute__((aligned(16))) float lds_v[2][64 * VS];
 
-  if (b.app.wgs > 0 && int32_t(blockIdx.x) >= b.app.wg0) {
-    // a workgroup of an append carried by this launch
-    fused_append_wg(b.app, int32_t(blockIdx.x) - b.app.wg0);
-    return;
-  }
   int32_t sid;
   const int32_t item = work_item(b, blockIdx.x, sid);
   if (sid < 0) return;
@@ -243,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const BatchArgs b) {
 }  // namespace
 
 hipError_t launch_attn_f32(const BatchArgs& b, int32_t head_dim, bool transient, hipStream_t stream) {
-  const dim3 grid(8 * b.items_per_xcd + b.app.wgs), block(kThreads);
+  const dim3 grid(8 * b.items_per_xcd), block(kThreads);
   if (head_dim == 64 && transient)
     hipLaunchKernelGGL((attn_f32_kernel<64, true>), grid, block, 0, stream, b);
   else if (head_dim == 64)

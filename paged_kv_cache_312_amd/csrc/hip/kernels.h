@@ -45,10 +45,11 @@ struct RowtabArgs {
   const StepDesc* desc;       // graph-replayed step: kv_len, patch_tokens from here (the
                               // grid covers the table's capacity)
   // Plan of lbm_append_run: positions [kv_len, kv_len + own_rows) are the
-  // step's own rows (frame-major, own_T = P + own_S tokens a frame), which the
-  // run reads from the caller's rows; their codes are the rows' destinations
-  // in the pools, the last frames' patch pages of the table and the last
-  // special tokens of the special stream.  0 otherwise.
+  // step's own rows (frame-major, own_T = P + own_S tokens a frame), which
+  // each block's append writes before its attention reads them; their codes
+  // are the rows' destinations in the pools, the last frames' patch pages of
+  // the table and the last special tokens of the special stream (padding
+  // repeats the first own row when no other key is visible).  0 otherwise.
   int32_t own_rows, own_T, own_S;
   float inv_T;
 };
@@ -75,10 +76,6 @@ struct AttnArgs {
   const void* tv;
   int32_t tr_start;
   int32_t row_bytes;          // H * D * element size
-  // lbm_append_run (16-bit kernels): the workgroups of query group 0 also
-  // store the own rows they stage, from LDS into the rows' pages, whose
-  // codes the row table holds at positions [tr_start, kv_len).
-  int32_t own_store;
   // Graph-replayed step: kv_len, n_tiles and tiles_per_split come from here
   // (num_splits stays the capture's; splits left without keys write empty
   // partials).
@@ -97,32 +94,12 @@ struct AttnArgs {
 // launch's item range, each stream's laid out as a single-stream launch's.
 constexpr int kMaxBatch = 8;
 
-// An append carried by an fp32 attention launch: workgroups [wg0, wg0 + wgs)
-// of the grid copy one block's rows of the step into their pages, with the
-// placement of append_scatter_kernel, instead of computing attention.  The
-// launch's attention reads those rows from k / v (the skip-append address
-// form), so no workgroup reads a row that another one writes.  wgs = 0: none
-// (the 16-bit kernels store the rows from the tiles they stage instead:
-// AttnArgs::own_store).
-struct FusedAppend {
-  const uint4* k;             // [rows][rc]
-  const uint4* v;
-  uint4* patch_pool;          // [pages][2][P][rc]
-  uint4* special_pool;        // [pages][2][SPS][rc]
-  const StepDesc* desc;       // st0, sp_first and the step's pages
-  int32_t rows;               // nf * T
-  int32_t T, P, S, SPS;
-  int32_t rc;                 // 16-byte chunks per token row
-  int32_t wg0, wgs;
-};
-
 struct BatchArgs {
   int32_t n;
   int32_t total_items;        // item_start[n]
   int32_t items_per_xcd;      // ceil(total_items / 8)
   int32_t item_start[kMaxBatch + 1];
   AttnArgs s[kMaxBatch];
-  FusedAppend app;
 };
 
 // Query rows per workgroup: the 16-bit kernel (8 wavefronts x 64) and the

@@ -67,15 +67,17 @@ __global__ void rowtab_kernel(RowtabArgs a) {
     a.n_pos = a.desc->n_tiles * 64;
   }
   if (j >= a.n_pos) return;
-  // with no key from the tables (every key of the step the frame's own), the
-  // padding positions take row 0 of patch page 0
+  // padding positions repeat a written row: the first visible key, else the
+  // first own row (lbm_append_run's plan, written by the block's append
+  // before its attention), else row 0 of patch page 0 (a skip-append step,
+  // whose kernel reads the padding from the caller's rows)
   uint32_t code;
   if (j < a.kv_len)
     code = row_code(a, j);
   else if (j - a.kv_len < a.own_rows)
     code = own_code(a, j - a.kv_len);
   else
-    code = a.kv_len > 0 ? row_code(a, 0) : 0u;
+    code = a.kv_len > 0 ? row_code(a, 0) : (a.own_rows > 0 ? own_code(a, 0) : 0u);
   a.rowtab[j] = code;
 }
 

@@ -1,12 +1,12 @@
 """lbm_append_run: one block's append and attention of a frame step in one
-launch.  The attention is checked against the oracle (dense softmax over the
+call.  The attention is checked against the oracle (dense softmax over the
 rule-derived visible set, the step's own rows included) on every output of
 small streams and on sampled rows of the ViT-L-shaped single-block stream; the
 bookkeeping against the reference allocator after every step; the pools by
 reading every visible row back through the table, byte for byte against the
-inputs (the rows the launches wrote: the fp32 kernel's extra workgroups, the
-16-bit kernels' query group 0 from the tiles it stages); and the protocol
-errors, which leave the cache as it was."""
+inputs (the rows each call's append wrote, which its attention then read
+back through the plan's own positions); and the protocol errors, which leave
+the cache as it was."""
 import numpy as np
 import pytest
 import torch
@@ -25,7 +25,7 @@ pytestmark = pytest.mark.gpu
                                  ODD_NO_SPECIAL], ids=lambda c: c.name)
 def test_small_streams_fused_every_output(cfg, splits):
     """Every step fused, every block and output checked (the first step's
-    frames have no earlier key: all of its keys come from the caller's rows)."""
+    frames have no earlier key: all of its keys are the step's own rows)."""
     n = len(workloads.step_schedule(cfg))
     w = run_stream(cfg, num_splits=splits, fused_steps=range(n), label=f"fused {cfg.name}")
     say(f"{cfg.name} splits={splits}: worst max_abs {w['max_abs']:.3e}, splits {sorted(w['splits'])}")
@@ -53,10 +53,8 @@ def test_vitl_single_block_fused():
                          ids=["tiny_f32", "small_bf16", "small_f16", "small_bf16_wide"])
 def test_fused_append_gather_back_is_byte_exact(cfg):
     """After each fused step, the rows the table points at are the input rows,
-    byte for byte, in visible order (scale, window, specials): written by the
-    fp32 kernel's extra workgroups, or by the 16-bit kernels' query group 0
-    from the tiles it stages (the wide case: own rows over several tiles and
-    key ranges)."""
+    byte for byte, in visible order (scale, window, specials) (the wide
+    case: own rows over several tiles and key ranges)."""
     from oracle import rules
     cache, _ = make_cache(cfg)
     T, P = cfg.tokens_per_frame, cfg.patches_per_frame
@@ -85,11 +83,10 @@ def test_fused_append_gather_back_is_byte_exact(cfg):
 
 @pytest.mark.parametrize("nq", [1, 33, 300])
 def test_fused_step_with_fewer_queries(nq):
-    """lbm_append_run with fewer query rows than the step has own rows: the
-    workgroups of query group 0 then hold few rows (wavefronts without any
-    take the load-only path) yet still store every own row.  Each output
-    against the oracle's dense softmax over the visible set built from the
-    input rows (own rows included), and the stored rows byte for byte."""
+    """lbm_append_run with fewer query rows than the step has own rows
+    (wavefronts without rows take the load-only path).  Each output against
+    the oracle's dense softmax over the visible set built from the input rows
+    (own rows included), and the stored rows byte for byte."""
     from oracle import attention, rules
     cfg = SMALL_BF16.replace(name="small_bf16_wide", patches_per_frame=300, num_heads=4)
     cache, _ = make_cache(cfg)
