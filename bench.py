@@ -122,9 +122,9 @@ def _traffic_record():
 
 
 def recorded_traffic():
-    """HBM bytes per lbm_append_run (append, attention and merge) from the
-    traffic record, or None if it is missing or was measured on other kernel
-    sources."""
+    """HBM bytes of one block's attention and merge (the roofline's kernels)
+    from the traffic record, or None if it is missing or was measured on other
+    kernel sources."""
     rec = _traffic_record()
     if rec is None or rec.get("kernel_source_hash") != kernel_source_hash():
         return None
@@ -197,15 +197,17 @@ def pmc_summary(fetch_dir, write_dir):
     f_scale = COPY_BYTES / (f["copy_kib"] * 1024.0)
     w_scale = COPY_BYTES / (w["copy_kib"] * 1024.0)
 
-    def per_call(x):
-        return (x["attn_kib"] + x["merge_kib"] * x["merges_per_attn"]
-                + x["run_append_kib"] * x["appends_per_attn"]) * 1024.0
+    def run_kib(x):     # the roofline's kernels: attention and merge
+        return x["attn_kib"] + x["merge_kib"] * x["merges_per_attn"]
 
-    fetch_b = per_call(f) * f_scale
-    write_b = per_call(w) * w_scale
+    fetch_b = run_kib(f) * 1024.0 * f_scale
+    write_b = run_kib(w) * 1024.0 * w_scale
+    call_b = (fetch_b + write_b + f["run_append_kib"] * f["appends_per_attn"] * 1024.0 * f_scale
+              + w["run_append_kib"] * w["appends_per_attn"] * 1024.0 * w_scale)
     rec = {"kernel_source_hash": kernel_source_hash(),
            "hbm_bytes_per_lbm_run": round(fetch_b + write_b),
            "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
+           "hbm_bytes_per_append_run": round(call_b),
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
            "raw_kib": out, "copy_bytes": COPY_BYTES}
     if f["append_kib"] is not None and w["append_kib"] is not None:
@@ -216,8 +218,9 @@ def pmc_summary(fetch_dir, write_dir):
                    append_fetch_bytes=round(a_fetch), append_write_bytes=round(a_write))
     os.makedirs(os.path.dirname(TRAFFIC_RECORD), exist_ok=True)
     with open(TRAFFIC_RECORD, "w") as fh:
-        fh.write("HBM traffic of one lbm_append_run (the block's append, attention, merge) and "
-                 "of one single-frame append, 24-block ViT-L step; written by "
+        fh.write("HBM traffic of the attention and merge of one block's call (hbm_bytes_per_lbm_run), "
+                 "of the whole lbm_append_run with its append (hbm_bytes_per_append_run) and of one "
+                 "single-frame append, 24-block ViT-L step; written by "
                  "'bench.py --pmc-summary' from two rocprofv3 --pmc runs of 'bench.py --steps 2 "
                  "--warmup 0 --no-cpu-baseline --no-variants --no-windows --calibrate-copy' (FETCH_SIZE, "
                  "then WRITE_SIZE)\n")
