@@ -26,9 +26,9 @@
 //    loads its share of each tile and keeps the barriers;
 //  * 64-key tiles of K and V go from HBM straight into LDS (row-major, global
 //    loads with an LDS destination, no staging registers) through rings of
-//    four stages each, three tiles ahead of use; one barrier per tile;
+//    four stages each, two tiles ahead of use; one barrier per two tiles;
 //  * the row codes that address those loads travel the same way, a ring of
-//    eight tiles' codes in LDS, three tiles further ahead, so that waiting for
+//    eight tiles' codes in LDS, two tiles further ahead, so that waiting for
 //    a code never waits for a newer tile;
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_{bf16,f16}: a lane then holds 16 scores of
 //    one query row per half, so the row max needs one exchange with lane +-32
@@ -123,16 +123,17 @@ constexpr int LS = 64;              // LDS row = one key's 64 columns, 128 bytes
 constexpr int TILE = 64 * LS;       // elements of one staged K or V tile
 constexpr int NST = 4;              // LDS stages of K and of V
 constexpr int NCODE = 2 * NST;      // LDS slots of row codes (64 per tile)
-constexpr int kLead = NST - 1;      // tiles whose K and V are loaded ahead of use
+// tiles whose K and V are loaded ahead of use: two fewer than the stages, so
+// that a wavefront one step ahead of another (steps between barriers) never
+// reloads a stage the other still reads
+constexpr int kLead = NST - 2;
 // Global loads (all with an LDS destination) each wavefront issues per tile:
 // one K, one V, then one of row codes.
 constexpr int kWaves = 8;              // wavefronts per workgroup
 constexpr int kThreads16 = 64 * kWaves;
 constexpr int kLoadsKV = 2;
 constexpr int kLoadsPerStep = kLoadsKV + 1;
-// Loads a wavefront may leave outstanding at the end of a step: this step's
-// and, in the first step, the prologue's loads of position kLead-1.
-constexpr int kInFlight = kLoadsPerStep + kLoadsKV;
+static_assert(kLead == 2, "the barrier after odd steps waits for the tile two steps ahead");
 static_assert(NCODE > 2 * kLead, "a code slot is reloaded only after its read");
 
 // s_waitcnt with only the vector-memory count constrained (expcnt and
@@ -396,22 +397,29 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
     asm volatile("" ::: "memory");
   };
   // Step i's loads: K and V of position i+kLead (into the stage read in step
-  // i-1, with the codes read at the end of step i-1) and the codes of
-  // position i+2kLead.  At the end of step i the wavefront waits until at
-  // most kInFlight of its loads are outstanding: position i+1's K and V and
-  // position i+kLead+1's codes have then landed (issued in step i+1-kLead or,
-  // for the first steps, in the prologue); those codes are read before the
-  // barrier, so their LDS latency overlaps it.
+  // i-2, with the codes read at the end of step i-1) and the codes of
+  // position i+2kLead.  At the end of step i the wavefront reads the codes
+  // of position i+1+kLead (loaded in step i-1), after waiting for them.
   uint32_t code_nx;  // code of this thread's row of the position the next step loads
   auto step_loads = [&](int32_t i, auto tr_c) __attribute__((always_inline)) {
     load_kv(tr_c, i + kLead, code_nx);
     load_codes(i + 2 * kLead);
   };
-  auto end_step = [&](int32_t i) __attribute__((always_inline)) {
-    LBM_WAIT_VMCNT_LDS0(kInFlight);
+  // A barrier after odd steps only: before it every wavefront waits for the
+  // K and V it loaded this step (position i+2), so that steps i+1 and i+2
+  // both find their tiles whole; between barriers a wavefront runs at most
+  // one step ahead of another, and its loads go to the stage read two steps
+  // earlier (every wavefront finished that step before the last barrier).
+  // After even steps the wait only covers the codes read here.  `odd` is a
+  // constant in the unrolled loop.
+  auto end_step = [&](int32_t i, bool odd) __attribute__((always_inline)) {
+    if (odd)
+      LBM_WAIT_VMCNT_LDS0(1);
+    else
+      LBM_WAIT_VMCNT_LDS0(kLoadsPerStep);
     asm volatile("" ::: "memory");  // the code reads below stay after the wait
     code_nx = codes_of(i + 1 + kLead);
-    barrier();
+    if (odd) barrier();
   };
   // the first step whose tile holds own rows (skip-append step)
   const int32_t own_i0 = a.tr_start / 64 - t_begin;
@@ -734,14 +742,15 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
     pv_block(nh_c, V, 1, pb);
   };
   // Prologue: row codes of positions 0 .. 2kLead-1, then K and V of
-  // positions 0 .. kLead-1; position 0 resident before the first step.
+  // positions 0 .. kLead-1, all resident before the first step (steps 0 and 1
+  // run before the first barrier).
 #pragma unroll
   for (int x = 0; x < 2 * kLead; ++x) load_codes(x);
   LBM_WAIT_VMCNT(0);
   asm volatile("" ::: "memory");  // the code reads below stay after the wait
 #pragma unroll
   for (int x = 0; x < kLead; ++x) load_kv(tr, x, codes_of(x));
-  LBM_WAIT_VMCNT_LDS0(kLoadsKV * (kLead - 1));
+  LBM_WAIT_VMCNT_LDS0(0);
   barrier();
   code_nx = codes_of(kLead);
 
@@ -749,16 +758,16 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
   // loads without the test for it.
   const int32_t n_plain = !TR || own_i0 >= n_t ? n_t : max(own_i0 - kLead + 1, 0);
   // The same barriers on every wavefront: one after the prologue and one
-  // after each step but the last.
+  // after each odd step but the last.
   if (idle) {
     int32_t i = 0;
     for (; i + 1 < n_plain; ++i) {
       step_loads(i, std::false_type{});
-      end_step(i);
+      end_step(i, (i & 1) != 0);
     }
     for (; i + 1 < n_t; ++i) {
       step_loads(i, tr);
-      end_step(i);
+      end_step(i, (i & 1) != 0);
     }
     LBM_WAIT_VMCNT(0);
     return;
@@ -771,7 +780,7 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
     }
     step_loads(0, tr);
     tile(nh_c, 0, true, false, 0);
-    end_step(0);
+    end_step(0, false);
     // NST steps per iteration, so that each tile's stage (i mod NST, with
     // i = 1 mod NST at the top) is a constant and its LDS operand addresses
     // fold into the instructions' offsets
@@ -791,7 +800,7 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
           __builtin_amdgcn_sched_barrier(0);
           step_loads(i + k, tr_c);
           tile(nh_c, i + k, false, false, st, kf0);
-          end_step(i + k);
+          end_step(i + k, (st & 1) != 0);
         }
       }
     };
@@ -800,7 +809,7 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
     for (; i + 1 < n_t; ++i) {
       step_loads(i, tr);
       tile(nh_c, i, false, false, i & (NST - 1));
-      end_step(i);
+      end_step(i, (i & 1) != 0);
     }
     tile(nh_c, n_t - 1, false, true, (n_t - 1) & (NST - 1));
   };
