@@ -18,12 +18,14 @@
 //    key range (split), one workgroup per CU (two wavefronts per SIMD); each
 //    wavefront owns up to 64 rows as two halves of 32, so every K and V
 //    operand read from LDS feeds two MFMAs, and each tile loaded into LDS
-//    serves all 512 rows.  The step's 32-row halves are dealt evenly to the
-//    query groups (1375 rows: 15 halves in the first group, 14 in the other
-//    two), so the groups that share a key range do equal work and stay in
-//    step on its tiles in L2.  A
-//    wavefront with one half computes that half only; one without rows only
-//    loads its share of each tile and keeps the barriers;
+//    serves all the group's rows.  The step's 32-row halves are dealt evenly
+//    to the query groups, whose number the planner chooses with the key
+//    ranges (1375 rows: 4 groups of 11, 11, 11 and 10 halves), so the groups
+//    that share a key range do equal work and stay in step on its tiles in
+//    L2; within a group the halves go to the SIMDs first (a step lasts as
+//    long as the busiest SIMD).  A wavefront with one half computes that half
+//    only; one without rows only loads its share of each tile and keeps the
+//    barriers;
 //  * 64-key tiles of K and V go from HBM straight into LDS (row-major, global
 //    loads with an LDS destination, no staging registers) through rings of
 //    four stages each, two tiles ahead of use; one barrier per two tiles;
