@@ -121,7 +121,7 @@ def run_stream(cfg: workloads.StreamConfig, check_steps: Optional[Iterable[int]]
     frames) are skip-append frames: planned and run with the frame's own rows,
     never appended; the bookkeeping must not move.  Steps in ``fused_steps``
     go through lbm_append_run (append, plan, evict and attention of each block
-    in one call and one launch).  Returns error statistics."""
+    in one call).  Returns error statistics."""
     skip = set(skip_steps)
     fused = set(fused_steps)
     sched = workloads.step_schedule(cfg)
