@@ -298,6 +298,10 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
   // a wavefront without rows (a group of fewer than 7 halves, at small Tq)
   // only loads its share of every tile and keeps the workgroup's barriers
   const bool idle = nh == 0;
+  // A SIMD's step lasts as long as its two wavefronts' work; the one with two
+  // halves has the longer stream, so its instructions go first when both are
+  // ready (0.6% faster in A/B; the other way round, 2.9% slower).
+  if (nh == 2) __builtin_amdgcn_s_setprio(2);
 
   // Q as the B operand of S^T = K Q^T: half h's row, columns 16ks + 8hh ..
   // +7, pre-multiplied by log2(e)/sqrt(D) (rounded to T) so that the MFMA
