@@ -300,8 +300,12 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
   const bool idle = nh == 0;
   // A SIMD's step lasts as long as its two wavefronts' work; the one with two
   // halves has the longer stream, so its instructions go first when both are
-  // ready (0.6% faster in A/B; the other way round, 2.9% slower).
+  // ready (0.6% faster in A/B; the other way round, 2.9% slower).  A
+  // wavefront without rows issues only its share of the tile loads, which
+  // every wavefront waits for at the next barrier: it goes first of all
+  // (another 0.6–1.2%).
   if (nh == 2) __builtin_amdgcn_s_setprio(2);
+  else if (nh == 0) __builtin_amdgcn_s_setprio(3);
 
   // Q as the B operand of S^T = K Q^T: half h's row, columns 16ks + 8hh ..
   // +7, pre-multiplied by log2(e)/sqrt(D) (rounded to T) so that the MFMA
