@@ -135,6 +135,7 @@ constexpr int kWaves = 8;              // wavefronts per workgroup
 constexpr int kThreads16 = 64 * kWaves;
 constexpr int kLoadsKV = 2;
 constexpr int kLoadsPerStep = kLoadsKV + 1;
+constexpr int kLoadsPerStepAll = 8 * kLoadsKV + 1;  // the loading wavefront's (every row)
 static_assert(kLead == 2, "the barrier after odd steps waits for the tile two steps ahead");
 static_assert(NCODE > 2 * kLead, "a code slot is reloaded only after its read");
 
@@ -260,6 +261,7 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
   const int32_t base = n_half / a.n_qt, rem = n_half - base * a.n_qt;
   const int32_t g_halves = base + (qt < rem ? 1 : 0);
   int32_t nh, qrow0;
+  bool one_loader;
   {
     const int32_t L = (g_halves + 3) / 4, e = 4 * L - g_halves;
     int32_t c[4] = {L, L, L, L};
@@ -275,6 +277,8 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
     const int32_t cs = sm == 0 ? c[0] : sm == 1 ? c[1] : sm == 2 ? c[2] : c[3];
     nh = __builtin_amdgcn_readfirstlane(min(max(cs - 2 * hi, 0), 2));
     qrow0 = 32 * (base * qt + min(qt, rem) + S + 2 * hi) + l32;
+    // the last wavefront holds no rows when SIMD 3 holds at most two halves
+    one_loader = __builtin_amdgcn_readfirstlane(c[3] <= 2 ? 1 : 0) != 0;
   }
   if (t_end <= t_begin) {
     // a split left without keys (graph-replayed steps keep the capture's split
@@ -295,9 +299,16 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
     }
     return;
   }
-  // a wavefront without rows (a group of fewer than 7 halves, at small Tq)
-  // only loads its share of every tile and keeps the workgroup's barriers
+  // a wavefront without rows (at most two halves on its SIMD) only loads and
+  // keeps the workgroup's barriers
   const bool idle = nh == 0;
+  // Loads into LDS: when the last wavefront holds no rows it issues every
+  // row's loads of every tile (and the row codes), and the others none, so
+  // that the wavefronts with rows spend no instruction on loads (0.4–1.2%
+  // faster in A/B); otherwise every wavefront loads its share (its 8 rows of
+  // each tile).
+  const bool all_rows = one_loader && wave == kWaves - 1;
+  const bool own_share = !one_loader;
   // A SIMD's step lasts as long as its two wavefronts' work; the one with two
   // halves has the longer stream, so its instructions go first when both are
   // ready (0.6% faster in A/B; the other way round, 2.9% slower).  A
@@ -331,10 +342,11 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
   }
 
   // Loads into LDS: a wavefront instruction fills 1 KB = 8 rows of 128 B,
-  // lane j writing row j/8, 16-byte slot j%8.  Wavefront w fills rows 8w..8w+7
-  // of each tile (key lp for thread tid, lp = tid/8), and slot lc of a row
-  // receives the row's chunk lc ^ swizzle, which places the tiles in the
-  // swizzled layout the operand reads expect.
+  // lane j writing row j/8, 16-byte slot j%8.  Sharing the loads, wavefront w
+  // fills rows 8w..8w+7 of each tile (key lp for thread tid, lp = tid/8); the
+  // loading wavefront fills all eight row blocks.  Slot lc of a row receives
+  // the row's chunk lc ^ swizzle, which places the tiles in the swizzled
+  // layout the operand reads expect.
   const int lc = tid & 7;
   const int lp = tid >> 3;
   const int32_t k_col = (head * D + ((lc ^ k_swz(lp)) * 8)) * 2;
@@ -397,6 +409,36 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
   auto codes_of = [&](int32_t x) __attribute__((always_inline)) {
     return lds_code[x & (NCODE - 1)][lp];
   };
+  // The loading wavefront (the last one, so its 8-row share is rows 56..63,
+  // whose K swizzle is the odd row blocks'): rows 8m + l/8, m = 0..7, of
+  // position x, from their codes c8[m]; the even row blocks' K chunks sit
+  // dk_even bytes from the odd ones' (the V swizzle is the same for all).
+  const int32_t dk_even = (head * D + ((lc ^ k_swz(lane >> 3)) * 8)) * 2 - k_col;
+  auto load_kv_all = [&](auto tr_c, int32_t x, const uint32_t* c8) __attribute__((always_inline)) {
+    const int32_t stage = x & (NST - 1);
+    const int32_t t0 = tile_at(x) * 64;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int32_t dk = (m & 1) ? 0 : dk_even;
+      const char* k0 = row_ptr(c8[m], false) + dk;
+      const char* v0 = row_ptr(c8[m], true);
+      if (decltype(tr_c)::value && t0 + 64 > a.tr_start) {
+        const int32_t j0 = t0 + 8 * m + (lane >> 3) - a.tr_start;
+        const int32_t n_own = a.kv_len - a.tr_start;
+        if (j0 >= 0) {
+          const int32_t j = min(j0, n_own - 1);
+          k0 = static_cast<const char*>(a.tk) + k_col + dk + size_t(j) * a.row_bytes;
+          v0 = static_cast<const char*>(a.tv) + v_col + size_t(j) * a.row_bytes;
+        }
+      }
+      load_to_lds<16>(k0, &lds_k[stage][(8 * m) * LS]);
+      load_to_lds<16>(v0, &lds_v[stage][(8 * m) * LS]);
+    }
+  };
+  auto codes_of_all = [&](int32_t x, uint32_t* c8) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) c8[m] = lds_code[x & (NCODE - 1)][8 * m + (lane >> 3)];
+  };
   // barrier without a memory fence (the fence would wait for every load
   // into LDS): each use follows an explicit wait for this wavefront's loads
   // into LDS that must have landed and for all its LDS reads, since the
@@ -428,7 +470,22 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
     else
       LBM_WAIT_VMCNT_LDS0(kLoadsPerStep);
     asm volatile("" ::: "memory");  // the code reads below stay after the wait
-    code_nx = codes_of(i + 1 + kLead);
+    if (own_share) code_nx = codes_of(i + 1 + kLead);
+    if (odd) barrier();
+  };
+  // the same for the loading wavefront: every row's codes and loads
+  uint32_t code8[8];
+  auto step_loads_all = [&](int32_t i, auto tr_c) __attribute__((always_inline)) {
+    load_kv_all(tr_c, i + kLead, code8);
+    load_codes(i + 2 * kLead);
+  };
+  auto end_step_all = [&](int32_t i, bool odd) __attribute__((always_inline)) {
+    if (odd)
+      LBM_WAIT_VMCNT_LDS0(1);
+    else
+      LBM_WAIT_VMCNT_LDS0(kLoadsPerStepAll);
+    asm volatile("" ::: "memory");  // the code reads below stay after the wait
+    codes_of_all(i + 1 + kLead, code8);
     if (odd) barrier();
   };
   // the first step whose tile holds own rows (skip-append step)
@@ -754,15 +811,26 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
   // Prologue: row codes of positions 0 .. 2kLead-1, then K and V of
   // positions 0 .. kLead-1, all resident before the first step (steps 0 and 1
   // run before the first barrier).
+  if (own_share || all_rows) {
 #pragma unroll
-  for (int x = 0; x < 2 * kLead; ++x) load_codes(x);
+    for (int x = 0; x < 2 * kLead; ++x) load_codes(x);
+  }
   LBM_WAIT_VMCNT(0);
   asm volatile("" ::: "memory");  // the code reads below stay after the wait
+  if (all_rows) {
 #pragma unroll
-  for (int x = 0; x < kLead; ++x) load_kv(tr, x, codes_of(x));
+    for (int x = 0; x < kLead; ++x) {
+      codes_of_all(x, code8);
+      load_kv_all(tr, x, code8);
+    }
+  } else if (own_share) {
+#pragma unroll
+    for (int x = 0; x < kLead; ++x) load_kv(tr, x, codes_of(x));
+  }
   LBM_WAIT_VMCNT_LDS0(0);
   barrier();
-  code_nx = codes_of(kLead);
+  if (all_rows) codes_of_all(kLead, code8);
+  if (own_share) code_nx = codes_of(kLead);
 
   // Steps before n_plain - 1 load no own row (kLead ahead): they take the
   // loads without the test for it.
@@ -771,13 +839,26 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
   // after each odd step but the last.
   if (idle) {
     int32_t i = 0;
-    for (; i + 1 < n_plain; ++i) {
-      step_loads(i, std::false_type{});
-      end_step(i, (i & 1) != 0);
-    }
-    for (; i + 1 < n_t; ++i) {
-      step_loads(i, tr);
-      end_step(i, (i & 1) != 0);
+    if (all_rows) {
+      for (; i + 1 < n_plain; ++i) {
+        step_loads_all(i, std::false_type{});
+        end_step_all(i, (i & 1) != 0);
+      }
+      for (; i + 1 < n_t; ++i) {
+        step_loads_all(i, tr);
+        end_step_all(i, (i & 1) != 0);
+      }
+    } else if (own_share) {
+      for (; i + 1 < n_plain; ++i) {
+        step_loads(i, std::false_type{});
+        end_step(i, (i & 1) != 0);
+      }
+      for (; i + 1 < n_t; ++i) {
+        step_loads(i, tr);
+        end_step(i, (i & 1) != 0);
+      }
+    } else {
+      for (; i + 1 < n_t; ++i) end_step(i, (i & 1) != 0);
     }
     LBM_WAIT_VMCNT(0);
     return;
@@ -788,7 +869,7 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
       tile(nh_c, 0, true, true, 0);
       return;
     }
-    step_loads(0, tr);
+    if (own_share) step_loads(0, tr);
     tile(nh_c, 0, true, false, 0);
     end_step(0, false);
     // NST steps per iteration, so that each tile's stage (i mod NST, with
@@ -808,7 +889,7 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
           const int st = (kStage0 + k) & (NST - 1);
           read_k(lds_k[st], 0, kf0);
           __builtin_amdgcn_sched_barrier(0);
-          step_loads(i + k, tr_c);
+          if (own_share) step_loads(i + k, tr_c);
           tile(nh_c, i + k, false, false, st, kf0);
           end_step(i + k, (st & 1) != 0);
         }
@@ -817,7 +898,7 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
     fast_steps(std::false_type{}, n_plain);
     if (TR) fast_steps(tr, n_t);
     for (; i + 1 < n_t; ++i) {
-      step_loads(i, tr);
+      if (own_share) step_loads(i, tr);
       tile(nh_c, i, false, false, i & (NST - 1));
       end_step(i, (i & 1) != 0);
     }
