@@ -205,7 +205,7 @@ __device__ __forceinline__ float round_up_to(float x) {
 
 // one kernel per element type: attn_d64_kernel<__bf16> and attn_d64_kernel<_Float16>;
 // TR: a skip-append step, whose last keys are the frame's own rows
-template <typename T, bool TR>
+template <typename T, bool TR, bool ONE>
 __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs b) {
   typedef typename Elt<T>::v8 h8;
   typedef typename Elt<T>::v2 h2;
@@ -261,7 +261,6 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
   const int32_t base = n_half / a.n_qt, rem = n_half - base * a.n_qt;
   const int32_t g_halves = base + (qt < rem ? 1 : 0);
   int32_t nh, qrow0;
-  bool one_loader;
   {
     const int32_t L = (g_halves + 3) / 4, e = 4 * L - g_halves;
     int32_t c[4] = {L, L, L, L};
@@ -277,8 +276,6 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
     const int32_t cs = sm == 0 ? c[0] : sm == 1 ? c[1] : sm == 2 ? c[2] : c[3];
     nh = __builtin_amdgcn_readfirstlane(min(max(cs - 2 * hi, 0), 2));
     qrow0 = 32 * (base * qt + min(qt, rem) + S + 2 * hi) + l32;
-    // the last wavefront holds no rows when SIMD 3 holds at most two halves
-    one_loader = __builtin_amdgcn_readfirstlane(c[3] <= 2 ? 1 : 0) != 0;
   }
   if (t_end <= t_begin) {
     // a split left without keys (graph-replayed steps keep the capture's split
@@ -302,13 +299,15 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
   // a wavefront without rows (at most two halves on its SIMD) only loads and
   // keeps the workgroup's barriers
   const bool idle = nh == 0;
-  // Loads into LDS: when the last wavefront holds no rows it issues every
-  // row's loads of every tile (and the row codes), and the others none, so
-  // that the wavefronts with rows spend no instruction on loads (0.4–1.2%
-  // faster in A/B); otherwise every wavefront loads its share (its 8 rows of
-  // each tile).
-  const bool all_rows = one_loader && wave == kWaves - 1;
-  const bool own_share = !one_loader;
+  // Loads into LDS (ONE: the launch's groups hold at most 11 halves each, so
+  // the dealing leaves every group's last wavefront without rows): the last
+  // wavefront issues every row's loads of every tile (and the row codes),
+  // and the others none, so that the wavefronts with rows spend no
+  // instruction on loads (0.4–1.2% faster in A/B at 4 groups of 10 and 11
+  // halves).  Otherwise every wavefront loads its share (its 8 rows of each
+  // tile).
+  constexpr bool own_share = !ONE;
+  const bool all_rows = ONE && wave == kWaves - 1;
   // A SIMD's step lasts as long as its two wavefronts' work; the one with two
   // halves has the longer stream, so its instructions go first when both are
   // ready (0.6% faster in A/B; the other way round, 2.9% slower).  A
@@ -951,24 +950,40 @@ __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs
 
 }  // namespace
 
+template <typename T>
+static void launch_inst(const BatchArgs& b, bool one, dim3 grid, dim3 block, hipStream_t stream) {
+  if (one)
+    hipLaunchKernelGGL((attn_d64_kernel<T, false, true>), grid, block, 0, stream, b);
+  else
+    hipLaunchKernelGGL((attn_d64_kernel<T, false, false>), grid, block, 0, stream, b);
+}
+
 hipError_t launch_attn16(const BatchArgs& b, int32_t head_dim, bool fp16, bool transient,
                          hipStream_t stream) {
   if (head_dim != 64) return hipErrorInvalidValue;
   const dim3 grid(8 * b.items_per_xcd), block(kThreads16);
+  // the single loading wavefront when every stream's largest query group
+  // holds at most 11 halves (the kernel deals them as ceil(halves / groups));
+  // not on skip-append steps, whose instance would then spill registers
+  bool one = !transient;
+  for (int32_t i = 0; i < b.n; ++i) {
+    const int32_t n_half = (b.s[i].Tq + 31) / 32;
+    one = one && (n_half + b.s[i].n_qt - 1) / b.s[i].n_qt <= 11;
+  }
   if (fp16 && transient)
-    hipLaunchKernelGGL((attn_d64_kernel<_Float16, true>), grid, block, 0, stream, b);
+    hipLaunchKernelGGL((attn_d64_kernel<_Float16, true, false>), grid, block, 0, stream, b);
   else if (fp16)
-    hipLaunchKernelGGL((attn_d64_kernel<_Float16, false>), grid, block, 0, stream, b);
+    launch_inst<_Float16>(b, one, grid, block, stream);
   else if (transient)
-    hipLaunchKernelGGL((attn_d64_kernel<__bf16, true>), grid, block, 0, stream, b);
+    hipLaunchKernelGGL((attn_d64_kernel<__bf16, true, false>), grid, block, 0, stream, b);
   else
-    hipLaunchKernelGGL((attn_d64_kernel<__bf16, false>), grid, block, 0, stream, b);
+    launch_inst<__bf16>(b, one, grid, block, stream);
   return hipGetLastError();
 }
 
 int32_t attn_occupancy16() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_d64_kernel<__bf16, false>, kThreads16, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_d64_kernel<__bf16, false, false>, kThreads16, 0) !=
           hipSuccess ||
       n < 1)
     return 1;
