@@ -24,8 +24,12 @@
 //    that share a key range do equal work and stay in step on its tiles in
 //    L2; within a group the halves go to the SIMDs first (a step lasts as
 //    long as the busiest SIMD).  A wavefront with one half computes that half
-//    only; one without rows only loads its share of each tile and keeps the
-//    barriers;
+//    only; one without rows only loads and keeps the barriers.  When every
+//    group leaves its last wavefront without rows (at most 11 halves a
+//    group), that wavefront issues all the tile loads and the others none;
+//    otherwise each wavefront loads its 8 rows of every tile.  Wavefronts
+//    with two halves, and above them the loading ones, run at raised
+//    priority;
 //  * 64-key tiles of K and V go from HBM straight into LDS (row-major, global
 //    loads with an LDS destination, no staging registers) through rings of
 //    four stages each, two tiles ahead of use; one barrier per two tiles;
@@ -204,7 +208,9 @@ __device__ __forceinline__ float round_up_to(float x) {
 }
 
 // one kernel per element type: attn_d64_kernel<__bf16> and attn_d64_kernel<_Float16>;
-// TR: a skip-append step, whose last keys are the frame's own rows
+// TR: a skip-append step, whose last keys are the frame's own rows; ONE: every
+// query group holds at most 11 halves, and each workgroup's last wavefront
+// (then without rows) issues all the tile loads
 template <typename T, bool TR, bool ONE>
 __global__ __launch_bounds__(kThreads16, 1) void attn_d64_kernel(const BatchArgs b) {
   typedef typename Elt<T>::v8 h8;
